@@ -1,0 +1,257 @@
+"""Benchmark of the ternary linear layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  decode  (qkv layer, K=5120 -> N=10240) for b = 1, 4, 8 and 16 tokens:
+          block rotation -> GEMV activation prep -> GEMV weight stream;
+  prefill (512-token chunk) for gate_up (5120 -> 34816) and down (17408 -> 5120):
+          block rotation -> per-token int8 quantisation -> int8 GEMM + rescale.
+Weights are packed once (load time, not timed) and cloned into rotating copies
+(>= 1 GiB per layer type) so that successive launches read weights that are not
+resident in the 256 MB Infinity Cache.
+
+Reported: decode GEMV GB/s (algorithmic bytes / kernel time, aggregated over the
+four batch sizes) as `value`, its fraction of the 8 TB/s HBM peak, prefill int8
+TOP/s against the 5.0 POP/s dense int8 peak, and the CPU oracle timed on a
+bounded sample.  Kernel durations come from HIP events recorded on the stream
+the kernels run on (torch's current stream) around each launch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
+MALL_BYTES = 256 * 2 ** 20
+ROTATE_BYTES = 2 ** 30
+
+DECODE_BS = (1, 4, 8, 16)
+PREFILL_M = 512
+
+
+def gemv_bytes(b, K, N):
+    """Algorithmic bytes of one GEMV weight-stream launch: packed codes, scales,
+    the two int8 activation limbs, and the bf16 output."""
+    return N * K // 4 + N * (K // 128) * 2 + 2 * b * K + 2 * b * N
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the "
+              "single-GPU kernels; multi-GPU sharding is design-only.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_gemv_gemm_amd as tl
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tl.lib()
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- weights (packed once, cloned into rotating copies) ----------------
+    def make_layer(config, li, K, N):
+        L = synth.LayerInputs(0, config, li, K, N)
+        codes = L.codes_torch(dev)
+        scales = torch.from_numpy(L.scales()).to(dev)
+        packed, q, rs = tl.pack_weights(codes, scales)
+        del codes
+        per = packed.numel() * 4 + scales.numel() * 2 + q.numel() + rs.numel() * 4
+        R = max(2, math.ceil(ROTATE_BYTES / per))
+        copies = [(packed, scales, q, rs)] + [(packed.clone(), scales.clone(), q.clone(), rs.clone())
+                                              for _ in range(R - 1)]
+        return copies
+
+    log("packing qkv (config 1) and prefill layers (config 3)")
+    qkv = make_layer(1, 0, 5120, 10240)
+    gate_up = make_layer(3, 0, 5120, 34816)
+    down = make_layer(3, 1, 17408, 5120)
+    torch.cuda.synchronize()
+    log(f"rotating copies: qkv {len(qkv)}, gate_up {len(gate_up)}, down {len(down)}")
+
+    # ---------------- activations ----------------
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    Kq, Nq = 5120, 10240
+    x_dec = {b: bf16(synth.activations(0, 1, 0, b, Kq)) for b in DECODE_BS}
+    xr_dec = {b: torch.empty((b, Kq), dtype=torch.float32, device=dev) for b in DECODE_BS}
+    ws_dec = {b: torch.empty((tl.gemv_workspace_size(b, Kq, Nq),), dtype=torch.uint8, device=dev)
+              for b in DECODE_BS}
+    y_dec = {b: torch.empty((b, Nq), dtype=torch.bfloat16, device=dev) for b in DECODE_BS}
+
+    pre = {}
+    for name, copies, li, K, N in (("gate_up", gate_up, 0, 5120, 34816), ("down", down, 1, 17408, 5120)):
+        pre[name] = dict(copies=copies, K=K, N=N,
+                         x=bf16(synth.activations(0, 3, li, PREFILL_M, K)),
+                         xr=torch.empty((PREFILL_M, K), dtype=torch.float32, device=dev),
+                         xq=torch.empty((PREFILL_M, K), dtype=torch.int8, device=dev),
+                         sx=torch.empty((PREFILL_M,), dtype=torch.float32, device=dev),
+                         y=torch.empty((PREFILL_M, N), dtype=torch.bfloat16, device=dev))
+
+    stream = torch.cuda.current_stream(dev)
+    rot = {"qkv": 0, "gate_up": 0, "down": 0}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step(rec):
+        """One pass of the hot path; appends (kind, key, start, end) events when rec is a list."""
+        for b in DECODE_BS:
+            packed, scales, _, _ = qkv[rot["qkv"] % len(qkv)]
+            rot["qkv"] += 1
+            tl.hadamard_blk(x_dec[b], out=xr_dec[b])
+            tl.gemv_prepare(xr_dec[b], ws_dec[b])
+            if rec is not None:
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+            tl.gemv_prepared(ws_dec[b], b, Kq, packed, scales, y_dec[b])
+            if rec is not None:
+                e1.record(stream)
+                rec.append(("gemv", b, e0, e1))
+        for name in ("gate_up", "down"):
+            P = pre[name]
+            packed, _, q, rs = P["copies"][rot[name] % len(P["copies"])]
+            rot[name] += 1
+            tl.hadamard_blk(P["x"], out=P["xr"])
+            tl.quant_act_int8(P["xr"], P["xq"], P["sx"])
+            if rec is not None:
+                e0, e1 = ev(), ev()
+                e0.record(stream)
+            tl.gemm_int8_rescale(P["xq"], P["sx"], packed, q, rs, out=P["y"])
+            if rec is not None:
+                e1.record(stream)
+                rec.append(("gemm", name, e0, e1))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    rec = []
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(rec)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    gemv_ms = {b: [] for b in DECODE_BS}
+    gemm_ms = {"gate_up": [], "down": []}
+    for kind, key, e0, e1 in rec:
+        (gemv_ms if kind == "gemv" else gemm_ms)[key].append(e0.elapsed_time(e1))
+
+    by_b = {}
+    tot_bytes = tot_s = 0.0
+    for b in DECODE_BS:
+        t = float(np.mean(gemv_ms[b])) * 1e-3
+        nbytes = gemv_bytes(b, Kq, Nq)
+        by_b[str(b)] = {"us": round(t * 1e6, 3), "GBps": round(nbytes / t / 1e9, 1),
+                        "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        tot_bytes += nbytes
+        tot_s += t
+    dec_gbs = tot_bytes / tot_s / 1e9
+
+    pre_out = {}
+    ops_tot = t_tot = 0.0
+    for name in ("gate_up", "down"):
+        t = float(np.mean(gemm_ms[name])) * 1e-3
+        ops = 2.0 * PREFILL_M * pre[name]["K"] * pre[name]["N"]
+        pre_out[name] = {"us": round(t * 1e6, 2), "TOPs": round(ops / t / 1e12, 1),
+                         "frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)}
+        ops_tot += ops
+        t_tot += t
+    pre_tops = ops_tot / t_tot / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle decode qkv b=16")
+        cpu = cpu_baseline(args.cpu_seconds)
+
+    out = {
+        "metric": "decode GEMV HBM GB/s (% of peak) at 5120→10240 b=1..16; prefill int8 TOPS",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "ternary linear layer: decode qkv K=5120 N=10240 at b=1,4,8,16 "
+                               "+ prefill M=512 gate_up 5120->34816 and down 17408->5120",
+                   "decode_b": list(DECODE_BS), "prefill_tokens": PREFILL_M,
+                   "rotating_weight_bytes": ROTATE_BYTES},
+        "decode_gemv_by_b": by_b,
+        "prefill_tops": round(pre_tops, 1),
+        "prefill_gemm": pre_out,
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": tl_kernel_name_for_gemv()},
+        "roofline_prefill": {"bound": "mfma", "achieved": round(pre_tops, 1), "peak": INT8_PEAK_TOPS,
+                             "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def tl_kernel_name_for_gemv():
+    return "gemv_i8x2_rb4_w8"
+
+
+def cpu_baseline(seconds):
+    """The oracle (numpy binary64) on the decode qkv layer at b=16, repeated for ~`seconds`."""
+    import oracle
+    import synth
+    try:
+        import threadpoolctl
+        cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
+    except Exception:
+        cores = os.cpu_count()
+    L = synth.LayerInputs(0, 1, 0, 5120, 10240)
+    codes, scales = L.codes(), L.scales()
+    x = synth.bf16_bits_to_f32(L.x(16))
+    reps, t = 0, 0.0
+    while t < seconds or reps == 0:
+        s = time.perf_counter()
+        oracle.gemv_ternary(oracle.rotate_exact(x), codes, scales)
+        t += time.perf_counter() - s
+        reps += 1
+    per = t / reps
+    return {"value": round(gemv_bytes(16, 5120, 10240) / per / 1e9, 3), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"decode qkv K=5120 N=10240 b=16 (rotation + GEMV), {reps} reps, {per * 1e3:.1f} ms each"}
+
+
+if __name__ == "__main__":
+    main()

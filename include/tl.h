@@ -1,0 +1,193 @@
+/*
+ * tl.h -- C ABI of the ternary linear-layer library for AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the quantized linear layer of the ternary 27B model described in
+ * qiita.com/nakanokensetsu/items/ecc183fae033565af7cb (cited below as [P1] with
+ * its section headings):
+ *   - weights are 2-bit codes in {-1, 0, +1} with one fp16 scale per row and per
+ *     128-element group along K ([P1] "前提");
+ *   - the input is rotated by a block-wise Sylvester Hadamard transform with
+ *     1024-wide blocks and an optional sign table ([P1] "前提", "1. TP=2 への移植");
+ *   - decode computes y = W (H_blk x) for 1..16 tokens;
+ *   - prefill decomposes each scale as q = round(127 s / smax) so that
+ *     code * q is exact in int8, quantises the rotated activations to int8 per
+ *     token, and runs one int8 x int8 -> int32 GEMM followed by a per-row and
+ *     per-token rescale ([P1] "4. 効いた高速化").
+ *
+ * Conventions for every call
+ *   - Every tensor argument is a DEVICE pointer owned by the caller, dense and
+ *     row-major (C order).  The library allocates no device memory; scratch, when
+ *     a call needs it, is a caller-provided workspace whose size a *_workspace_size
+ *     query returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *     work is enqueued on it; no call synchronises.  A device fault surfaces at the
+ *     caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is launched.  A failed
+ *     check returns a non-zero TL_ERR_* code, launches nothing and leaves every
+ *     output untouched.  Launch failures return TL_ERR_LAUNCH.
+ *   - Counts of zero (T, b, M, N) are valid and do nothing; K must be positive.
+ *   - Inputs and outputs must not overlap (TL_ERR_ALIAS).
+ *   - Pointers must be 16-byte aligned (TL_ERR_ALIGN).
+ *   - Value preconditions (codes in {-1,0,+1}, signs +-1, finite inputs) are not
+ *     checked on the device, except that tl_pack_weights can count bad codes.
+ *   - Calls are thread-safe; concurrent calls on different streams are
+ *     independent (each uses only its own arguments and workspace).
+ *
+ * Packed weight layout (ABI version 1; the page gives no layout, this one is ours)
+ *   packed is uint32 [N, K/16].  Word w of row n holds the codes of
+ *   k = 16 w + j, j = 0..15.  Code j occupies bits 8*(j mod 4) + 2*(j div 4) and
+ *   the bit above it, so byte b of the word holds codes j = b, b+4, b+8, b+12 in
+ *   its bit pairs 0..3.  A field is the code's two's-complement low two bits:
+ *   0 -> 00, +1 -> 01, -1 -> 11 (10 is never written).  With this order,
+ *   ((w >> 2r) & 0x03030303) holds codes 4r..4r+3 in bytes 0..3, in k order.
+ */
+#ifndef TL_H
+#define TL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TL_ABI_VERSION 1
+
+/* status codes returned by every call */
+#define TL_OK 0
+#define TL_ERR_NULLPTR 1     /* a required pointer is NULL */
+#define TL_ERR_SHAPE 2       /* a size is negative, out of range or not a required multiple */
+#define TL_ERR_ALIGN 3       /* a pointer is not 16-byte aligned */
+#define TL_ERR_DTYPE 4       /* y_dtype is not TL_BF16 or TL_F32 */
+#define TL_ERR_LAUNCH 5      /* the HIP runtime reported an error */
+#define TL_ERR_UNSUPPORTED 6 /* no kernel variant for this request */
+#define TL_ERR_WORKSPACE 7   /* workspace missing or smaller than the query says */
+#define TL_ERR_ALIAS 8       /* an output overlaps an input or another output */
+
+/* output element types */
+#define TL_BF16 0 /* bfloat16, round to nearest even from fp32 */
+#define TL_F32 1  /* IEEE binary32 */
+
+/* Version of the packed layout and of the signatures below (TL_ABI_VERSION). */
+int tl_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *tl_status_string(int status);
+
+/* Name of the last kernel this host thread launched through the library
+ * ("" before the first launch).  Used to check which variant ran. */
+const char *tl_last_kernel_name(void);
+
+/*
+ * tl_pack_weights -- load-time conversion of one ternary layer.
+ *   [P1] "前提" (2-bit codes, one fp16 scale per row and 128-group) and
+ *   [P1] "4. 効いた高速化" (q[n,g] = round(127 s[n,g] / smax[n])).
+ * in  codes      int8   [N, K]     values in {-1, 0, +1}
+ * in  scales     fp16   [N, K/128] (raw IEEE half bits), finite
+ * out packed     uint32 [N, K/16]  layout above
+ * out q          int8   [N, K/128] q = RNE( fl32(fl32(127*s) / smax) ),
+ *                                  smax[n] = max_g |s[n,g]|; |q| <= 127
+ * out row_scale  f32    [N]        fl32(smax / 127)
+ * out invalid_count int32 [1] or NULL: if not NULL, the number of codes outside
+ *                  {-1,0,+1} is ADDED to it (the caller zeroes it first).
+ * A row whose scales are all zero gets q = 0 and row_scale = 0.
+ * Requires K > 0, K % 128 == 0.
+ */
+int tl_pack_weights(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                    uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
+                    void *stream);
+
+/*
+ * tl_hadamard_blk -- block rotation of the layer input.
+ *   [P1] "前提" (Hadamard rotation on the input side) and "1. TP=2 への移植"
+ *   (Sylvester type, 1024-wide blocks, sign table keyed by the layer width).
+ * in  x      bf16 [T, K] (raw bits)
+ * in  signs  int8 [K] of +-1, or NULL for all +1; applied to x before H
+ * out xr     f32  [T, K]: for each token and block j,
+ *            xr[t, 1024 j + i] = (1/32) sum_m (-1)^popcount(i & m) d[1024 j + m] x[t, 1024 j + m]
+ *            computed exactly (binary64 butterflies) and rounded once to f32.
+ *            The result is exact before that rounding whenever the x values are
+ *            multiples of 2^-31 below 2^8 in magnitude (bf16 with |x| >= 2^-24).
+ * Requires K > 0, K % 1024 == 0.
+ */
+int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, float *xr,
+                    void *stream);
+
+/*
+ * tl_gemv_ternary -- decode GEMV, y = W xr for 1..16 tokens.
+ *   [P1] "前提" (y = W (H_blk x), W = code * group scale).
+ * in  xr      f32    [b, K]      rotated activations (tl_hadamard_blk output)
+ * in  packed  uint32 [N, K/16]   from tl_pack_weights
+ * in  scales  fp16   [N, K/128]
+ * out y       [b, N] of y_dtype: y[t,n] = sum_g s[n,g] sum_{k in g} code[n,k] xr[t,k]
+ * workspace   device scratch of at least tl_gemv_workspace_size(b, K, N) bytes,
+ *             16-byte aligned; its contents on entry do not matter.
+ * Numerics: each weight is read once for all b tokens; group sums run on int8
+ * matrix cores with each token's activations held as a 15-bit fixed-point value
+ * split into two int8 limbs (scale amax_t / 32639), and group results are
+ * accumulated in f32.  Relative Frobenius error against exact arithmetic is
+ * about 3e-5 on the generator's data (bound used by the tests: 1e-3).
+ * Requires 0 <= b <= 16, K > 0, K % 128 == 0.
+ */
+size_t tl_gemv_workspace_size(int64_t b, int64_t K, int64_t N);
+int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint32_t *packed,
+                    const uint16_t *scales, void *y, int y_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * The two stages of tl_gemv_ternary, for callers that apply several weight
+ * matrices to the same rotated input (e.g. q/k/v or gate/up as separate
+ * layers) or that time the stages apart:
+ *   tl_gemv_prepare  writes the activation limbs and token scales of xr [b, K]
+ *                    into the workspace (one kernel);
+ *   tl_gemv_prepared runs the weight-streaming kernel on a workspace that
+ *                    tl_gemv_prepare filled for the same b and K (one kernel).
+ * tl_gemv_ternary(...) is exactly tl_gemv_prepare followed by tl_gemv_prepared.
+ * The workspace must stay unmodified between the two calls.
+ */
+int tl_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
+                    size_t workspace_bytes, void *stream);
+int tl_gemv_prepared(const void *workspace, size_t workspace_bytes, int64_t b, int64_t K,
+                     int64_t N, const uint32_t *packed, const uint16_t *scales, void *y,
+                     int y_dtype, void *stream);
+
+/*
+ * tl_quant_act_int8 -- per-token int8 quantisation of rotated activations.
+ *   [P1] "4. 効いた高速化" (activations quantised to int8 per token after the
+ *   rotation, which evens out outliers).
+ * in  xr         f32  [T, K]
+ * out xq         int8 [T, K]  clamp( RNE( fl32(xr / sx_t) ), -127, 127 )
+ * out tok_scale  f32  [T]     sx_t = fl32(amax_t / 127), amax_t = max_k |xr[t,k]|
+ * A token with amax = 0 gets sx = 0 and xq = 0.  Divisions are correctly rounded.
+ * Requires K > 0, K % 128 == 0.
+ */
+int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
+                      void *stream);
+
+/*
+ * tl_gemm_int8_rescale -- prefill int8 GEMM and rescale.
+ *   [P1] "4. 効いた高速化" (W_int8 = code * q exactly in int8; one int8 GEMM,
+ *   then a per-row and per-token rescale).
+ * in  xq         int8   [M, K]     from tl_quant_act_int8
+ * in  tok_scale  f32    [M]
+ * in  packed     uint32 [N, K/16]  from tl_pack_weights
+ * in  q          int8   [N, K/128] from tl_pack_weights
+ * in  row_scale  f32    [N]        from tl_pack_weights
+ * out y          [M, N] of y_dtype: y = fl32( fl32(acc) * row_scale[n] ) * tok_scale[m]
+ * out acc_out    int32  [M, N] or NULL: acc[m,n] = sum_k xq[m,k] code[n,k] q[n,k/128]
+ *                (exact; |acc| <= K * 127^2, so K <= 133143 keeps it in int32)
+ * workspace      device scratch of at least tl_gemm_workspace_size(M, K, N)
+ *                bytes (may be NULL when that size is 0).
+ * Requires K > 0, K % 128 == 0, K <= 133120.
+ */
+size_t tl_gemm_workspace_size(int64_t M, int64_t K, int64_t N);
+int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K,
+                         int64_t N, const uint32_t *packed, const int8_t *q,
+                         const float *row_scale, void *y, int y_dtype, int32_t *acc_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TL_H */

@@ -1,0 +1,269 @@
+"""Python binding of libtl, the ternary linear-layer library for MI355X (gfx950).
+
+The functions mirror the C ABI in include/tl.h one to one.  They only check
+tensor dtypes/devices/contiguity, allocate outputs with torch when none are
+given, and pass raw pointers and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if
+libtl.so is missing or a call fails, a RuntimeError is raised.
+
+Method: qiita.com/nakanokensetsu/items/ecc183fae033565af7cb ("前提",
+"1. TP=2 への移植", "4. 効いた高速化").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtl.so")
+
+TL_BF16, TL_F32 = 0, 1
+GROUP, HBLOCK = 128, 1024
+
+_lib = None
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/tl.h
+_SIGS = {
+    "tl_abi_version": (ctypes.c_int, []),
+    "tl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tl_last_kernel_name": (ctypes.c_char_p, []),
+    "tl_pack_weights": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "tl_hadamard_blk": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "tl_gemv_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
+    "tl_gemv_ternary": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_int,
+                                       _c_p, _c_sz, _c_p]),
+    "tl_gemv_prepare": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_sz, _c_p]),
+    "tl_gemv_prepared": (ctypes.c_int, [_c_p, _c_sz, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_int,
+                                        _c_p]),
+    "tl_quant_act_int8": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "tl_gemm_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
+    "tl_gemm_int8_rescale": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
+                                            ctypes.c_int, _c_p, _c_p, _c_sz, _c_p]),
+}
+
+
+def lib():
+    """The loaded libtl.so (ctypes), with argument types declared."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().tl_status_string(s).decode()
+
+
+def last_kernel_name() -> str:
+    return lib().tl_last_kernel_name().decode()
+
+
+def abi_version() -> int:
+    return lib().tl_abi_version()
+
+
+def _check(name: str, status: int):
+    if status != 0:
+        raise RuntimeError(f"{name} failed: {status_string(status)} (status {status})")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device=None):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _out_code(dtype):
+    import torch
+    if dtype == torch.bfloat16:
+        return TL_BF16
+    if dtype == torch.float32:
+        return TL_F32
+    raise TypeError("output dtype must be torch.bfloat16 or torch.float32")
+
+
+# ---------------------------------------------------------------------------
+# the five calls
+# ---------------------------------------------------------------------------
+def pack_weights(codes, scales, packed=None, q=None, row_scale=None, invalid_count=None):
+    """codes int8 [N,K], scales fp16 [N,K/128] -> (packed int32 [N,K/16], q int8 [N,K/128],
+    row_scale f32 [N]).  ``packed`` holds the uint32 words (torch has no uint32 math)."""
+    import torch
+    _need(codes, "codes", torch.int8, 2)
+    _need(scales, "scales", torch.float16, 2)
+    N, K = codes.shape
+    dev = codes.device
+    packed = torch.empty((N, K // 16), dtype=torch.int32, device=dev) if packed is None else packed
+    q = torch.empty((N, K // GROUP), dtype=torch.int8, device=dev) if q is None else q
+    row_scale = torch.empty((N,), dtype=torch.float32, device=dev) if row_scale is None else row_scale
+    _need(packed, "packed", torch.int32, 2)
+    _need(q, "q", torch.int8, 2)
+    _need(row_scale, "row_scale", torch.float32, 1)
+    if invalid_count is not None:
+        _need(invalid_count, "invalid_count", torch.int32, 1)
+    if scales.shape != (N, K // GROUP) or packed.shape != (N, K // 16) or q.shape != (N, K // GROUP) \
+            or row_scale.shape != (N,):
+        raise ValueError("shape mismatch in pack_weights")
+    _check("tl_pack_weights", lib().tl_pack_weights(
+        _ptr(codes), _ptr(scales), N, K, _ptr(packed), _ptr(q), _ptr(row_scale), _ptr(invalid_count),
+        _stream(dev)))
+    return packed, q, row_scale
+
+
+def hadamard_blk(x, signs=None, out=None):
+    """x bf16 [T,K] -> xr f32 [T,K]: exact block rotation (1/32) H1024 (d * x), rounded once."""
+    import torch
+    _need(x, "x", torch.bfloat16, 2)
+    T, K = x.shape
+    if signs is not None:
+        _need(signs, "signs", torch.int8, 1)
+        if signs.shape != (K,):
+            raise ValueError("signs must be [K]")
+    out = torch.empty((T, K), dtype=torch.float32, device=x.device) if out is None else out
+    _need(out, "out", torch.float32, 2)
+    if out.shape != (T, K):
+        raise ValueError("out must be [T, K]")
+    _check("tl_hadamard_blk", lib().tl_hadamard_blk(_ptr(x), T, K, _ptr(signs), _ptr(out), _stream(x.device)))
+    return out
+
+
+def gemv_workspace_size(b: int, K: int, N: int) -> int:
+    return int(lib().tl_gemv_workspace_size(b, K, N))
+
+
+def gemv_ternary(xr, packed, scales, out_dtype=None, out=None, workspace=None):
+    """xr f32 [b,K] (b <= 16), packed [N,K/16], scales fp16 [N,K/128] -> y [b,N]."""
+    import torch
+    _need(xr, "xr", torch.float32, 2)
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    b, K = xr.shape
+    N = packed.shape[0]
+    if packed.shape != (N, K // 16) or scales.shape != (N, K // GROUP):
+        raise ValueError("shape mismatch in gemv_ternary")
+    if out is None:
+        out = torch.empty((b, N), dtype=out_dtype or torch.bfloat16, device=xr.device)
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    if out.shape != (b, N):
+        raise ValueError("out must be [b, N]")
+    need = gemv_workspace_size(b, K, N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=xr.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check("tl_gemv_ternary", lib().tl_gemv_ternary(
+        _ptr(xr), b, K, N, _ptr(packed), _ptr(scales), _ptr(out), code, _ptr(workspace),
+        workspace.numel(), _stream(xr.device)))
+    return out
+
+
+def gemv_prepare(xr, workspace):
+    """First stage of gemv_ternary: activation limbs of xr f32 [b,K] into ``workspace``."""
+    import torch
+    _need(xr, "xr", torch.float32, 2)
+    _need(workspace, "workspace", torch.uint8, 1)
+    b, K = xr.shape
+    _check("tl_gemv_prepare", lib().tl_gemv_prepare(_ptr(xr), b, K, _ptr(workspace), workspace.numel(),
+                                                    _stream(xr.device)))
+    return workspace
+
+
+def gemv_prepared(workspace, b, K, packed, scales, out):
+    """Second stage of gemv_ternary: y [b,N] from a workspace filled by gemv_prepare(b, K)."""
+    import torch
+    _need(workspace, "workspace", torch.uint8, 1)
+    _need(packed, "packed", torch.int32, 2)
+    _need(scales, "scales", torch.float16, 2)
+    N = packed.shape[0]
+    if packed.shape != (N, K // 16) or scales.shape != (N, K // GROUP) or out.shape != (b, N):
+        raise ValueError("shape mismatch in gemv_prepared")
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    _check("tl_gemv_prepared", lib().tl_gemv_prepared(
+        _ptr(workspace), workspace.numel(), b, K, N, _ptr(packed), _ptr(scales), _ptr(out), code,
+        _stream(out.device)))
+    return out
+
+
+def quant_act_int8(xr, xq=None, tok_scale=None):
+    """xr f32 [T,K] -> (xq int8 [T,K], tok_scale f32 [T])."""
+    import torch
+    _need(xr, "xr", torch.float32, 2)
+    T, K = xr.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device=xr.device) if xq is None else xq
+    tok_scale = torch.empty((T,), dtype=torch.float32, device=xr.device) if tok_scale is None else tok_scale
+    _need(xq, "xq", torch.int8, 2)
+    _need(tok_scale, "tok_scale", torch.float32, 1)
+    if xq.shape != (T, K) or tok_scale.shape != (T,):
+        raise ValueError("shape mismatch in quant_act_int8")
+    _check("tl_quant_act_int8", lib().tl_quant_act_int8(_ptr(xr), T, K, _ptr(xq), _ptr(tok_scale),
+                                                        _stream(xr.device)))
+    return xq, tok_scale
+
+
+def gemm_workspace_size(M: int, K: int, N: int) -> int:
+    return int(lib().tl_gemm_workspace_size(M, K, N))
+
+
+def gemm_int8_rescale(xq, tok_scale, packed, q, row_scale, out_dtype=None, out=None, acc_out=None,
+                      want_acc=False, workspace=None):
+    """xq int8 [M,K], tok_scale f32 [M], packed/q/row_scale from pack_weights -> y [M,N]
+    (and the exact int32 accumulator when ``want_acc`` or ``acc_out`` is given)."""
+    import torch
+    _need(xq, "xq", torch.int8, 2)
+    _need(tok_scale, "tok_scale", torch.float32, 1)
+    _need(packed, "packed", torch.int32, 2)
+    _need(q, "q", torch.int8, 2)
+    _need(row_scale, "row_scale", torch.float32, 1)
+    M, K = xq.shape
+    N = packed.shape[0]
+    if tok_scale.shape != (M,) or packed.shape != (N, K // 16) or q.shape != (N, K // GROUP) \
+            or row_scale.shape != (N,):
+        raise ValueError("shape mismatch in gemm_int8_rescale")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=xq.device)
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    if out.shape != (M, N):
+        raise ValueError("out must be [M, N]")
+    if acc_out is None and want_acc:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    if acc_out is not None:
+        _need(acc_out, "acc_out", torch.int32, 2)
+        if acc_out.shape != (M, N):
+            raise ValueError("acc_out must be [M, N]")
+    need = gemm_workspace_size(M, K, N)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=xq.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check("tl_gemm_int8_rescale", lib().tl_gemm_int8_rescale(
+        _ptr(xq), _ptr(tok_scale), M, K, N, _ptr(packed), _ptr(q), _ptr(row_scale), _ptr(out), code,
+        _ptr(acc_out), _ptr(workspace), ws_bytes, _stream(xq.device)))
+    return (out, acc_out) if acc_out is not None else out

@@ -1,0 +1,209 @@
+// Host side of the C ABI declared in include/tl.h: argument checks, then launches.
+// Every check runs before any HIP call, so a rejected call touches neither the
+// GPU nor the outputs.
+#include <stdint.h>
+#include <string.h>
+
+#include "tl_internal.h"
+
+namespace tl {
+static thread_local const char *g_last_kernel = "";
+void set_last_kernel(const char *name) { g_last_kernel = name; }
+}  // namespace tl
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  const void *p;
+  size_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// outputs must not overlap inputs or each other
+bool any_alias(const Span *in, int nin, const Span *out, int nout) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlap(out[o], in[i])) return true;
+    for (int j = o + 1; j < nout; ++j)
+      if (overlap(out[o], out[j])) return true;
+  }
+  return false;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? TL_OK : TL_ERR_LAUNCH; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;  // rows, tokens and K stay below 2^31
+
+}  // namespace
+
+extern "C" {
+
+int tl_abi_version(void) { return TL_ABI_VERSION; }
+
+const char *tl_status_string(int s) {
+  switch (s) {
+    case TL_OK: return "ok";
+    case TL_ERR_NULLPTR: return "a required pointer is NULL";
+    case TL_ERR_SHAPE: return "invalid shape (negative, too large, or not a required multiple)";
+    case TL_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case TL_ERR_DTYPE: return "y_dtype must be TL_BF16 or TL_F32";
+    case TL_ERR_LAUNCH: return "HIP runtime error during launch";
+    case TL_ERR_UNSUPPORTED: return "no kernel variant for this request";
+    case TL_ERR_WORKSPACE: return "workspace missing or too small";
+    case TL_ERR_ALIAS: return "an output overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+const char *tl_last_kernel_name(void) { return tl::g_last_kernel; }
+
+int tl_pack_weights(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                    uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
+                    void *stream) {
+  if (N < 0 || K <= 0 || K % tl::kGroup || N >= kMaxDim || K >= kMaxDim) return TL_ERR_SHAPE;
+  if (N == 0) return TL_OK;
+  if (!codes || !scales || !packed || !q || !row_scale) return TL_ERR_NULLPTR;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(packed) || !aligned16(q) ||
+      !aligned16(row_scale))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  Span in[] = {{codes, size_t(N) * K}, {scales, size_t(N) * G * 2}};
+  Span out[] = {{packed, size_t(N) * (K / 16) * 4}, {q, size_t(N) * G}, {row_scale, size_t(N) * 4},
+                {invalid_count, invalid_count ? 4u : 0u}};
+  if (any_alias(in, 2, out, 4)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_pack(codes, scales, N, K, packed, q, row_scale, invalid_count,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, float *xr,
+                    void *stream) {
+  if (T < 0 || K <= 0 || K % tl::kHBlock || T >= kMaxDim || K >= kMaxDim) return TL_ERR_SHAPE;
+  if (T == 0) return TL_OK;
+  if (!x || !xr) return TL_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(xr) || (signs && !aligned16(signs))) return TL_ERR_ALIGN;
+  Span in[] = {{x, size_t(T) * K * 2}, {signs, signs ? size_t(K) : 0u}};
+  Span out[] = {{xr, size_t(T) * K * 4}};
+  if (any_alias(in, 2, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_hadamard(x, T, K, signs, xr, static_cast<hipStream_t>(stream)));
+}
+
+size_t tl_gemv_workspace_size(int64_t b, int64_t K, int64_t N) {
+  if (b < 0 || b > 16 || K <= 0 || K % tl::kGroup || N < 0) return 0;
+  return tl::gemv_workspace_bytes(b, K, N);
+}
+
+namespace {
+int check_gemv_shape(int64_t b, int64_t K, int64_t N) {
+  if (b < 0 || b > 16 || N < 0 || K <= 0 || K % tl::kGroup || N >= kMaxDim || K >= kMaxDim)
+    return TL_ERR_SHAPE;
+  return TL_OK;
+}
+}  // namespace
+
+int tl_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  if (int s = check_gemv_shape(b, K, 0)) return s;
+  if (b == 0) return TL_OK;
+  if (!xr) return TL_ERR_NULLPTR;
+  const size_t need = tl::gemv_workspace_bytes(b, K, 0);
+  if (!workspace || workspace_bytes < need) return TL_ERR_WORKSPACE;
+  if (!aligned16(xr) || !aligned16(workspace)) return TL_ERR_ALIGN;
+  Span in[] = {{xr, size_t(b) * K * 4}};
+  Span out[] = {{workspace, need}};
+  if (any_alias(in, 1, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_gemv_prepare(xr, b, K, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int tl_gemv_prepared(const void *workspace, size_t workspace_bytes, int64_t b, int64_t K, int64_t N,
+                     const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                     void *stream) {
+  if (int s = check_gemv_shape(b, K, N)) return s;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (b == 0 || N == 0) return TL_OK;
+  if (!packed || !scales || !y) return TL_ERR_NULLPTR;
+  const size_t need = tl::gemv_workspace_bytes(b, K, N);
+  if (!workspace || workspace_bytes < need) return TL_ERR_WORKSPACE;
+  if (!aligned16(packed) || !aligned16(scales) || !aligned16(y) || !aligned16(workspace))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(b) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{workspace, need}, {packed, size_t(N) * (K / 16) * 4}, {scales, size_t(N) * G * 2}};
+  Span out[] = {{y, ysz}};
+  if (any_alias(in, 3, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint32_t *packed,
+                    const uint16_t *scales, void *y, int y_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  if (int s = check_gemv_shape(b, K, N)) return s;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (b == 0 || N == 0) return TL_OK;
+  if (!xr || !packed || !scales || !y) return TL_ERR_NULLPTR;
+  const size_t need = tl::gemv_workspace_bytes(b, K, N);
+  if (!workspace || workspace_bytes < need) return TL_ERR_WORKSPACE;
+  if (!aligned16(xr) || !aligned16(packed) || !aligned16(scales) || !aligned16(y) ||
+      !aligned16(workspace))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(b) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{xr, size_t(b) * K * 4}, {packed, size_t(N) * (K / 16) * 4}, {scales, size_t(N) * G * 2}};
+  Span out[] = {{y, ysz}, {workspace, need}};
+  if (any_alias(in, 3, out, 2)) return TL_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = tl::launch_gemv_prepare(xr, b, K, workspace, st);
+  if (e != hipSuccess) return TL_ERR_LAUNCH;
+  return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype, st));
+}
+
+int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
+                      void *stream) {
+  if (T < 0 || K <= 0 || K % tl::kGroup || T >= kMaxDim || K >= kMaxDim) return TL_ERR_SHAPE;
+  if (T == 0) return TL_OK;
+  if (!xr || !xq || !tok_scale) return TL_ERR_NULLPTR;
+  if (!aligned16(xr) || !aligned16(xq) || !aligned16(tok_scale)) return TL_ERR_ALIGN;
+  Span in[] = {{xr, size_t(T) * K * 4}};
+  Span out[] = {{xq, size_t(T) * K}, {tok_scale, size_t(T) * 4}};
+  if (any_alias(in, 1, out, 2)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_quant(xr, T, K, xq, tok_scale, static_cast<hipStream_t>(stream)));
+}
+
+size_t tl_gemm_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 0 || K <= 0 || K % tl::kGroup) return 0;
+  return tl::gemm_workspace_bytes(M, K, N);
+}
+
+int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K,
+                         int64_t N, const uint32_t *packed, const int8_t *q,
+                         const float *row_scale, void *y, int y_dtype, int32_t *acc_out,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % tl::kGroup || K > 133120 || M >= kMaxDim || N >= kMaxDim)
+    return TL_ERR_SHAPE;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (M == 0 || N == 0) return TL_OK;
+  if (!xq || !tok_scale || !packed || !q || !row_scale || !y) return TL_ERR_NULLPTR;
+  const size_t need = tl::gemm_workspace_bytes(M, K, N);
+  if (need && (!workspace || workspace_bytes < need)) return TL_ERR_WORKSPACE;
+  if (!aligned16(xq) || !aligned16(tok_scale) || !aligned16(packed) || !aligned16(q) ||
+      !aligned16(row_scale) || !aligned16(y) || (acc_out && !aligned16(acc_out)) ||
+      (need && !aligned16(workspace)))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(M) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{xq, size_t(M) * K}, {tok_scale, size_t(M) * 4}, {packed, size_t(N) * (K / 16) * 4},
+               {q, size_t(N) * G}, {row_scale, size_t(N) * 4}};
+  Span out[] = {{y, ysz}, {acc_out, acc_out ? size_t(M) * N * 4 : 0u}, {workspace, need}};
+  if (any_alias(in, 5, out, 3)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_gemm(xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype,
+                                  acc_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tl.h"
+
+namespace tl {
+
+constexpr int kGroup = 128;   // weights per fp16 scale along K
+constexpr int kHBlock = 1024; // Hadamard block width
+
+// name of the last kernel launched by this host thread
+void set_last_kernel(const char *name);
+
+hipError_t launch_pack(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
+                       uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
+                       hipStream_t stream);
+
+hipError_t launch_hadamard(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs,
+                           float *xr, hipStream_t stream);
+
+hipError_t launch_quant(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
+                        hipStream_t stream);
+
+size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t N);
+hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
+                               hipStream_t stream);
+hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t N,
+                            const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                            hipStream_t stream);
+
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
+                       const uint32_t *packed, const int8_t *q, const float *row_scale, void *y,
+                       int y_dtype, int32_t *acc_out, void *workspace, hipStream_t stream);
+
+}  // namespace tl

@@ -1,0 +1,117 @@
+"""The C ABI library loads and exports what include/tl.h declares; host-side checks.
+
+No compute call reaches the GPU here: every call below is rejected by the
+library's host-side argument checks (or is a zero-size no-op) before any HIP
+runtime call, so these tests run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_gemv_gemm_amd as tl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tl.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tl.LIB_PATH), reason="libtl.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(tl_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert {"tl_pack_weights", "tl_hadamard_blk", "tl_gemv_ternary", "tl_quant_act_int8",
+            "tl_gemm_int8_rescale"} <= set(names)
+    L = ctypes.CDLL(tl.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    # the binding declares exactly the header's functions
+    assert set(tl._SIGS) == set(names)
+
+
+def test_version_and_status_strings():
+    assert tl.abi_version() == 1
+    for s in range(0, 9):
+        assert tl.status_string(s)
+    assert tl.status_string(0) == "ok"
+    assert tl.status_string(99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+FAKE2 = ctypes.c_void_p(0x20000000)
+FAKE3 = ctypes.c_void_p(0x40000000)
+FAKE4 = ctypes.c_void_p(0x60000000)
+FAKE5 = ctypes.c_void_p(0x80000000)
+ODD = ctypes.c_void_p(0x10004)
+
+
+def test_pack_rejections():
+    L = tl.lib()
+    assert L.tl_pack_weights(FAKE, FAKE2, 4, 100, FAKE3, FAKE4, FAKE5, None, None) == 2   # K % 128
+    assert L.tl_pack_weights(FAKE, FAKE2, -1, 128, FAKE3, FAKE4, FAKE5, None, None) == 2
+    assert L.tl_pack_weights(FAKE, FAKE2, 4, 0, FAKE3, FAKE4, FAKE5, None, None) == 2
+    assert L.tl_pack_weights(None, FAKE2, 4, 128, FAKE3, FAKE4, FAKE5, None, None) == 1
+    assert L.tl_pack_weights(ODD, FAKE2, 4, 128, FAKE3, FAKE4, FAKE5, None, None) == 3
+    assert L.tl_pack_weights(FAKE, FAKE2, 4, 128, FAKE, FAKE4, FAKE5, None, None) == 8   # packed aliases codes
+    assert L.tl_pack_weights(FAKE, FAKE2, 0, 128, FAKE3, FAKE4, FAKE5, None, None) == 0   # empty: no-op
+
+
+def test_hadamard_rejections():
+    L = tl.lib()
+    assert L.tl_hadamard_blk(FAKE, 2, 1536, None, FAKE2, None) == 2       # K % 1024
+    assert L.tl_hadamard_blk(FAKE, 2, 1024, None, None, None) == 1
+    assert L.tl_hadamard_blk(FAKE, 2, 1024, ODD, FAKE2, None) == 3        # signs misaligned
+    assert L.tl_hadamard_blk(FAKE, 2, 1024, None, FAKE, None) == 8
+    assert L.tl_hadamard_blk(FAKE, 0, 1024, None, FAKE2, None) == 0
+
+
+def test_gemv_rejections():
+    L = tl.lib()
+    ws = L.tl_gemv_workspace_size(4, 1024, 256)
+    assert ws >= 2 * 4 * 1024
+    assert L.tl_gemv_workspace_size(17, 1024, 256) == 0
+    args = lambda b=4, K=1024, N=256, y=FAKE4, dt=0, w=FAKE5, wb=ws: (FAKE, b, K, N, FAKE2, FAKE3, y, dt, w, wb, None)
+    assert L.tl_gemv_ternary(*args(b=17)) == 2
+    assert L.tl_gemv_ternary(*args(K=1000)) == 2
+    assert L.tl_gemv_ternary(*args(dt=7)) == 4
+    assert L.tl_gemv_ternary(*args(y=None)) == 1
+    assert L.tl_gemv_ternary(*args(w=None)) == 7
+    assert L.tl_gemv_ternary(*args(wb=ws - 1)) == 7
+    assert L.tl_gemv_ternary(*args(y=ODD)) == 3
+    assert L.tl_gemv_ternary(*args(y=FAKE)) == 8
+    assert L.tl_gemv_ternary(*args(b=0)) == 0
+    assert L.tl_gemv_ternary(*args(N=0)) == 0
+
+
+def test_quant_rejections():
+    L = tl.lib()
+    assert L.tl_quant_act_int8(FAKE, 3, 100, FAKE2, FAKE3, None) == 2
+    assert L.tl_quant_act_int8(FAKE, 3, 128, None, FAKE3, None) == 1
+    assert L.tl_quant_act_int8(FAKE, 3, 128, FAKE2, ODD, None) == 3
+    assert L.tl_quant_act_int8(FAKE, 3, 128, FAKE, FAKE3, None) == 8
+    assert L.tl_quant_act_int8(FAKE, 0, 128, FAKE2, FAKE3, None) == 0
+
+
+def test_gemm_rejections():
+    L = tl.lib()
+    args = lambda M=8, K=1024, N=256, y=FAKE4, dt=1, acc=None: (
+        FAKE, FAKE2, M, K, N, FAKE3, FAKE4, FAKE5, y, dt, acc, None, 0, None)
+    assert L.tl_gemm_int8_rescale(*args(K=133248)) == 2     # accumulator could overflow int32
+    assert L.tl_gemm_int8_rescale(*args(K=1000)) == 2
+    assert L.tl_gemm_int8_rescale(*args(dt=3)) == 4
+    assert L.tl_gemm_int8_rescale(*args(y=None)) == 1
+    assert L.tl_gemm_int8_rescale(*args(acc=ODD, y=ctypes.c_void_p(0xA0000000))) == 3
+    assert L.tl_gemm_int8_rescale(*args(y=FAKE)) == 8
+    assert L.tl_gemm_int8_rescale(*args(M=0)) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        tl.hadamard_blk(torch.zeros((1, 1024), dtype=torch.bfloat16))

@@ -1,0 +1,317 @@
+"""HIP path vs the CPU oracle, element by element, on seeded synthetic layers.
+
+Bars: bit-exact for packed words, q, row_scale, the rotation's f32 output (the
+rotation is exact before its single rounding), int8 activations, token scales
+and int32 accumulators; relative Frobenius error <= 1e-3 for floating-point
+outputs (f32 against the binary64 oracle, bf16 against the oracle rounded to
+bf16).  Every output is poisoned before the call.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import REL_TOL, Layer, announce, bf16_dev, dev, poison_, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tl():
+    import quantized_gemv_gemm_amd as tl
+    tl.lib()   # raises if the library is missing: no silent fallback
+    return tl
+
+
+# (config, layer index, K, N) of every layer shape in the workloads
+SHAPES = {
+    "tiny": (0, 0, 1024, 256),
+    "qkv": (1, 0, 5120, 10240),
+    "gate_up": (2, 0, 5120, 34816),
+    "down": (2, 1, 17408, 5120),
+}
+
+_layers = {}
+
+
+def layer(name, tl):
+    if name not in _layers:
+        c, li, K, N = SHAPES[name]
+        announce(f"build layer {name} K={K} N={N}")
+        _layers[name] = Layer(0, c, li, K, N, dev()).pack()
+    return _layers[name]
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "qkv", "gate_up", "down"])
+def test_pack_bit_exact(tl, name):
+    import torch
+    d = dev()
+    c, li, K, N = SHAPES[name]
+    L = Layer(0, c, li, K, N, d)
+    packed = poison_(torch.empty((N, K // 16), dtype=torch.int32, device=d))
+    q = poison_(torch.empty((N, K // 128), dtype=torch.int8, device=d))
+    rs = poison_(torch.empty((N,), dtype=torch.float32, device=d))
+    bad = torch.zeros((1,), dtype=torch.int32, device=d)
+    announce(f"tl_pack_weights {name} N={N} K={K}")
+    tl.pack_weights(L.codes_d, L.scales_d, packed, q, rs, invalid_count=bad)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), oracle.pack_codes(L.codes))
+    q_ref, rs_ref, _ = oracle.decompose_scales(L.scales)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(rs.cpu().numpy().view(np.uint32), rs_ref.view(np.uint32))
+    assert int(bad.item()) == 0
+    assert tl.last_kernel_name() == "pack_rows"
+
+
+def test_pack_edge_rows_and_bad_codes(tl):
+    import torch
+    d = dev()
+    rng = np.random.default_rng(12)
+    K, N = 256, 5
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, 2))).astype(np.float16)
+    scales[1] = 0.0                                   # zero row -> q = 0, row_scale = 0
+    scales[2] = [np.float16(0.25), np.float16(0.5)]   # exact tie 63.5 -> 64
+    scales[3] = [np.float16(-0.75), np.float16(0.5)]  # negative maximum magnitude
+    scales[4] = [np.float16(0.48828125), np.float16(0.9921875)]  # tie 62.5 -> 62
+    announce("tl_pack_weights edge rows")
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    q_ref, rs_ref, _ = oracle.decompose_scales(scales)
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(rs.cpu().numpy(), rs_ref)
+    assert q.cpu().numpy()[2, 0] == 64 and q.cpu().numpy()[4, 0] == 62
+    # invalid codes are counted
+    bad_codes = codes.copy()
+    bad_codes[0, 3], bad_codes[4, 100], bad_codes[2, 7] = 2, -2, 5
+    cnt = torch.zeros((1,), dtype=torch.int32, device=d)
+    tl.pack_weights(to_dev(bad_codes, d), to_dev(scales, d), invalid_count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == 3
+
+
+# ---------------------------------------------------------------------------
+# rotation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,K,with_signs", [(1, 1024, False), (16, 5120, False), (3, 17408, True),
+                                            (512, 17408, False), (7, 2048, True)])
+def test_hadamard_bit_exact(tl, T, K, with_signs):
+    import torch
+    d = dev()
+    xbits = synth.activations(0, 9, K, T, K)
+    signs = None
+    if with_signs:
+        signs = np.where(np.random.default_rng(K).random(K) < 0.5, -1, 1).astype(np.int8)
+    out = poison_(torch.empty((T, K), dtype=torch.float32, device=d))
+    announce(f"tl_hadamard_blk T={T} K={K} signs={with_signs}")
+    tl.hadamard_blk(bf16_dev(xbits, d), None if signs is None else to_dev(signs, d), out=out)
+    ref = oracle.rotate_f32(synth.bf16_bits_to_f32(xbits), signs)
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_hadamard_closed_form(tl):
+    """x = H e_m / 32 (entries +-1/32, exact in bf16) rotates to e_m."""
+    d = dev()
+    H = oracle.sylvester_hadamard(1024)
+    x = np.zeros((4, 2048), dtype=np.float32)
+    ms = [0, 5, 1023, 511]
+    for t, m in enumerate(ms):
+        x[t, 1024 * (t % 2):1024 * (t % 2) + 1024] = H[:, m] / 32.0
+    xr = tl.hadamard_blk(bf16_dev(synth.f32_to_bf16_bits(x), d)).cpu().numpy()
+    want = np.zeros_like(x)
+    for t, m in enumerate(ms):
+        want[t, 1024 * (t % 2) + m] = 1.0
+    np.testing.assert_array_equal(xr, want)
+
+
+# ---------------------------------------------------------------------------
+# activation quantisation
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,K", [(1, 1024), (512, 5120), (512, 17408), (5, 256)])
+def test_quant_bit_exact(tl, T, K):
+    import torch
+    d = dev()
+    rng = np.random.default_rng(T * 7 + K)
+    xr = (rng.standard_normal((T, K)) * np.exp(rng.standard_normal((T, 1)))).astype(np.float32)
+    if T > 2:
+        xr[1] = 0.0            # zero token
+        xr[2, 3] = 1e4         # one dominant value
+    xq = poison_(torch.empty((T, K), dtype=torch.int8, device=d))
+    sx = poison_(torch.empty((T,), dtype=torch.float32, device=d))
+    announce(f"tl_quant_act_int8 T={T} K={K}")
+    tl.quant_act_int8(to_dev(xr, d), xq, sx)
+    xq_ref, sx_ref = oracle.quant_act_int8(xr)
+    np.testing.assert_array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    np.testing.assert_array_equal(xq.cpu().numpy(), xq_ref)
+
+
+def test_quant_near_ties(tl):
+    """Rows whose values sit where x/sx and x*(127/amax) round apart."""
+    d = dev()
+    near = [(-0.74002606, 3.68562), (-1.5955694, 3.5241272), (0.5879848, 3.3188474), (1.9004934, 3.5235422)]
+    xr = np.zeros((4, 128), dtype=np.float32)
+    for r, (v, amax) in enumerate(near):
+        xr[r, 0], xr[r, 3] = np.float32(amax), np.float32(v)
+    xq, sx = tl.quant_act_int8(to_dev(xr, d))
+    xq_ref, sx_ref = oracle.quant_act_int8(xr)
+    np.testing.assert_array_equal(xq.cpu().numpy(), xq_ref)
+    np.testing.assert_array_equal(sx.cpu().numpy(), sx_ref)
+
+
+# ---------------------------------------------------------------------------
+# decode GEMV
+# ---------------------------------------------------------------------------
+def _gemv_case(tl, L, b, x_layer_cfg):
+    import torch
+    d = L.d
+    xbits = synth.activations(0, x_layer_cfg[0], x_layer_cfg[1], b, L.K)
+    x = bf16_dev(xbits, d)
+    xr = tl.hadamard_blk(x)
+    announce(f"tl_gemv_ternary b={b} K={L.K} N={L.N}")
+    y32 = poison_(torch.empty((b, L.N), dtype=torch.float32, device=d))
+    tl.gemv_ternary(xr, L.packed, L.scales_d, out=y32)
+    kname = tl.last_kernel_name()
+    y16 = poison_(torch.empty((b, L.N), dtype=torch.bfloat16, device=d))
+    tl.gemv_ternary(xr, L.packed, L.scales_d, out=y16)
+    torch.cuda.synchronize()
+    ref = oracle.gemv_ternary(oracle.rotate_exact(synth.bf16_bits_to_f32(xbits)), L.codes, L.scales)
+    e32 = oracle.rel_fro(y32.cpu().numpy(), ref)
+    e16 = oracle.rel_fro(y16.float().cpu().numpy(), oracle.bf16_round(ref))
+    announce(f"  rel_fro f32={e32:.3e} bf16={e16:.3e} kernel={kname}")
+    assert e32 <= REL_TOL and e16 <= REL_TOL, (e32, e16)
+    assert kname.startswith("gemv_")
+    return e32
+
+
+@pytest.mark.parametrize("name,b", [("tiny", 1), ("qkv", 1), ("qkv", 4), ("qkv", 8), ("qkv", 16),
+                                    ("gate_up", 1), ("gate_up", 16), ("down", 1), ("down", 16)])
+def test_gemv_parity(tl, name, b):
+    L = layer(name, tl)
+    c, li, _, _ = SHAPES[name]
+    _gemv_case(tl, L, b, (c, li))
+
+
+@pytest.mark.parametrize("K,N,b", [(128, 300, 3), (256, 17, 16), (1024, 1000, 5), (3072, 64, 2)])
+def test_gemv_ragged(tl, K, N, b):
+    """N not a multiple of the row tile, K smaller than the wave count, odd b."""
+    import torch
+    d = dev()
+    rng = np.random.default_rng(K + N + b)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    scales[N // 2] = 0
+    xr = rng.standard_normal((b, K)).astype(np.float32)
+    xr[b - 1, :] *= 1e-3
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    y = poison_(torch.empty((b, N), dtype=torch.float32, device=d))
+    announce(f"tl_gemv_ternary ragged K={K} N={N} b={b}")
+    tl.gemv_ternary(to_dev(xr, d), packed, to_dev(scales, d), out=y)
+    got = y.cpu().numpy()
+    ref = oracle.gemv_ternary(xr, codes, scales)
+    assert oracle.rel_fro(got, ref) <= REL_TOL
+    assert np.all(got[:, N // 2] == 0)
+    # each token row on its own (a tiny row must not drown in the others)
+    for t in range(b):
+        assert oracle.rel_fro(got[t], ref[t]) <= REL_TOL
+
+
+def test_gemv_zero_token(tl):
+    d = dev()
+    L = layer("tiny", tl)
+    xr = np.zeros((2, L.K), dtype=np.float32)
+    xr[1] = np.random.default_rng(13).standard_normal(L.K)
+    y = tl.gemv_ternary(to_dev(xr, d), L.packed, L.scales_d, out_dtype=__import__("torch").float32)
+    got = y.cpu().numpy()
+    assert np.all(got[0] == 0)
+    assert oracle.rel_fro(got[1], oracle.gemv_ternary(xr[1:], L.codes, L.scales)[0]) <= REL_TOL
+
+
+# ---------------------------------------------------------------------------
+# prefill int8 GEMM + rescale
+# ---------------------------------------------------------------------------
+def _gemm_check(tl, codes, scales, packed, q, rs, xq_np, sx_np, label):
+    import torch
+    d = packed.device
+    M, N = xq_np.shape[0], codes.shape[0]
+    y32 = poison_(torch.empty((M, N), dtype=torch.float32, device=d))
+    acc = poison_(torch.empty((M, N), dtype=torch.int32, device=d))
+    announce(f"tl_gemm_int8_rescale {label} M={M} K={codes.shape[1]} N={N}")
+    tl.gemm_int8_rescale(to_dev(xq_np, d), to_dev(sx_np, d), packed, q, rs, out=y32, acc_out=acc)
+    kname = tl.last_kernel_name()
+    y16 = poison_(torch.empty((M, N), dtype=torch.bfloat16, device=d))
+    tl.gemm_int8_rescale(to_dev(xq_np, d), to_dev(sx_np, d), packed, q, rs, out=y16)
+    torch.cuda.synchronize()
+    q_ref, rs_ref, _ = oracle.decompose_scales(scales)
+    acc_ref = oracle.gemm_int8_acc(xq_np, codes, q_ref)
+    np.testing.assert_array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    ref = oracle.rescale(acc_ref, rs_ref, sx_np)
+    e32 = oracle.rel_fro(y32.cpu().numpy(), ref)
+    e16 = oracle.rel_fro(y16.float().cpu().numpy(), oracle.bf16_round(ref))
+    announce(f"  acc bit-exact; rel_fro f32={e32:.3e} bf16={e16:.3e} kernel={kname}")
+    assert e32 <= REL_TOL and e16 <= REL_TOL
+    return acc
+
+
+@pytest.mark.parametrize("name,M", [("tiny", 1), ("tiny", 64), ("gate_up", 512), ("down", 512)])
+def test_prefill_path_parity(tl, name, M):
+    """rotation -> per-token int8 -> int8 GEMM + rescale, each stage checked."""
+    import torch
+    L = layer(name, tl)
+    c, li, K, N = SHAPES[name]
+    d = L.d
+    xbits = synth.activations(0, 3 if name != "tiny" else 0, li, M, K)
+    announce(f"prefill {name} M={M}: rotation + quant")
+    xr = tl.hadamard_blk(bf16_dev(xbits, d))
+    xq, sx = tl.quant_act_int8(xr)
+    torch.cuda.synchronize()
+    xr_ref = oracle.rotate_f32(synth.bf16_bits_to_f32(xbits))
+    np.testing.assert_array_equal(xr.cpu().numpy(), xr_ref)
+    xq_ref, sx_ref = oracle.quant_act_int8(xr_ref)
+    np.testing.assert_array_equal(xq.cpu().numpy(), xq_ref)
+    np.testing.assert_array_equal(sx.cpu().numpy(), sx_ref)
+    _gemm_check(tl, L.codes, L.scales, L.packed, L.q, L.rs, xq_ref, sx_ref, name)
+
+
+@pytest.mark.parametrize("M,K,N", [(77, 256, 300), (1, 128, 33), (130, 1024, 257), (129, 2048, 512)])
+def test_gemm_ragged(tl, M, K, N):
+    d = dev()
+    rng = np.random.default_rng(M * 31 + K + N)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.exp(rng.standard_normal(M)).astype(np.float32)
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "ragged")
+
+
+def test_gemm_extreme_accumulator(tl):
+    """All +-127 inputs and weights: |acc| = K * 127^2 at K = 17408 stays exact."""
+    d = dev()
+    K, N, M = 17408, 64, 4
+    codes = np.ones((N, K), dtype=np.int8)
+    codes[1::2] = -1
+    scales = np.ones((N, K // 128), dtype=np.float16)
+    xq = np.full((M, K), 127, dtype=np.int8)
+    xq[1] = -127
+    sx = np.ones(M, dtype=np.float32)
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    acc = _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "extreme")
+    assert int(acc[0, 0]) == K * 127 * 127 and int(acc[1, 0]) == -K * 127 * 127
+
+
+def test_int_outputs_deterministic(tl):
+    import torch
+    L = layer("qkv", tl)
+    d = L.d
+    rng = np.random.default_rng(14)
+    xq = to_dev(rng.integers(-127, 128, (40, L.K)).astype(np.int8), d)
+    sx = to_dev(np.ones(40, dtype=np.float32), d)
+    _, a1 = tl.gemm_int8_rescale(xq, sx, L.packed, L.q, L.rs, want_acc=True)
+    _, a2 = tl.gemm_int8_rescale(xq, sx, L.packed, L.q, L.rs, want_acc=True)
+    p2, q2, r2 = tl.pack_weights(L.codes_d, L.scales_d)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(p2, L.packed) and torch.equal(q2, L.q)
