@@ -78,6 +78,10 @@ const char *tl_status_string(int status);
  * ("" before the first launch).  Used to check which variant ran. */
 const char *tl_last_kernel_name(void);
 
+/* Text of the HIP runtime error behind the last TL_ERR_LAUNCH returned on this
+ * host thread ("" if none).  For diagnostics only. */
+const char *tl_last_error_detail(void);
+
 /*
  * tl_pack_weights -- load-time conversion of one ternary layer.
  *   [P1] "前提" (2-bit codes, one fp16 scale per row and 128-group) and

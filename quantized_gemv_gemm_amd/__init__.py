@@ -31,6 +31,7 @@ _SIGS = {
     "tl_abi_version": (ctypes.c_int, []),
     "tl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tl_last_kernel_name": (ctypes.c_char_p, []),
+    "tl_last_error_detail": (ctypes.c_char_p, []),
     "tl_pack_weights": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "tl_hadamard_blk": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "tl_gemv_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
@@ -52,6 +53,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        # One HIP runtime per process: torch ships its own libamdhip64 (needed as
+        # "libamdhip64.so"), libtl needs "libamdhip64.so.7".  Loading torch first makes
+        # the dynamic linker resolve libtl's dependency to torch's copy (same SONAME),
+        # so device memory, streams and kernels all live in one runtime.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(L, name)
@@ -74,7 +80,8 @@ def abi_version() -> int:
 
 def _check(name: str, status: int):
     if status != 0:
-        raise RuntimeError(f"{name} failed: {status_string(status)} (status {status})")
+        detail = lib().tl_last_error_detail().decode() if status == 5 else ""
+        raise RuntimeError(f"{name} failed: {status_string(status)} (status {status}) {detail}".rstrip())
 
 
 def _ptr(t):

@@ -35,10 +35,40 @@ constexpr int kAStride = kGroup + 16;  // LDS row pitch in bytes (padding spread
 
 static_assert(kBM * kGroup == kThreads * 4 * 16, "A stage = 4 x 16 bytes per thread");
 static_assert(kBN == 4 * 64, "4 waves x 64 columns");
+constexpr int kDepth = 4;  // groups of global loads in flight per thread
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+struct GemmStage {
+  v4u a[4];  // this thread's four 16-byte pieces of the 128 x 128 activation tile
+  v4u b[2];  // packed words 4h..4h+3 of the group for the lane's two weight columns
+  int q[2];  // q of those columns for the group
+};
 
 __device__ __forceinline__ uint32_t perm_table(int qv) {
   // bytes: [0] = 0, [1] = q, [2] = unused, [3] = -q
   return ((uint32_t)(uint8_t)(int8_t)(-qv) << 24) | ((uint32_t)(uint8_t)(int8_t)qv << 8);
+}
+
+// Loads are unconditional: rows past M and columns past N read a clamped, valid
+// address and their results are never stored.  With no divergent branches the
+// compiler can count outstanding loads exactly and keep kDepth groups in flight.
+__device__ __forceinline__ void load_stage(GemmStage &st, int g, const int8_t *const (&asrc)[4],
+                                           const char *const (&bsrc)[2],
+                                           const int8_t *const (&qsrc)[2]) {
+  const int64_t koff = int64_t(g) * kGroup;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const v4u *>(asrc[i] + koff);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    st.b[j] = *reinterpret_cast<const v4u *>(bsrc[j] + 32 * int64_t(g));
+    st.q[j] = (int)qsrc[j][g];
+  }
+}
+
+__device__ __forceinline__ void stage_to_lds(int8_t *buf, const GemmStage &st, const int (&adst)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u *>(buf + adst[i]) = st.a[i];
 }
 
 // 16 int8 weights code*q from one packed word, k order
@@ -49,6 +79,24 @@ __device__ __forceinline__ v4i expand_word(uint32_t w, uint32_t table) {
   r[2] = (int)__builtin_amdgcn_perm(0u, table, (w >> 4) & 0x03030303u);
   r[3] = (int)__builtin_amdgcn_perm(0u, table, (w >> 6) & 0x03030303u);
   return r;
+}
+
+// one 128-wide group: 4 k-steps x (4 x 2) MFMA 32x32x32 tiles for this wave
+__device__ __forceinline__ void gemm_group(const GemmStage &st, const int8_t *sbuf, int l32, int h,
+                                           v16i (&acc)[4][2]) {
+  const uint32_t tab0 = perm_table(st.q[0]), tab1 = perm_table(st.q[1]);
+  const int8_t *abase = sbuf + l32 * kAStride + 64 * h;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const v4i bf0 = expand_word(st.b[0][s], tab0);
+    const v4i bf1 = expand_word(st.b[1][s], tab1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const v4i af = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + 16 * s);
+      acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mt][0], 0, 0, 0);
+      acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mt][1], 0, 0, 0);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
@@ -66,25 +114,22 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
 
   // activation staging: chunk c = tid + 256 i -> row c/8, 16-byte column c%8
   const int8_t *asrc[4];
-  bool arow_ok[4];
   int adst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + kThreads * i;
     const int row = c >> 3, c16 = c & 7;
-    arow_ok[i] = m0 + row < M;
-    asrc[i] = xq + (arow_ok[i] ? (m0 + row) : 0) * K + 16 * c16;
+    const int64_t m = m0 + row < M ? m0 + row : M - 1;
+    asrc[i] = xq + m * K + 16 * c16;
     adst[i] = row * kAStride + 16 * c16;
   }
   // weight columns of this lane: one per 32-wide N tile
   const char *bsrc[2];
   const int8_t *qsrc[2];
-  bool bcol_ok[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t n = n0 + 64 * wave + 32 * j + l32;
-    bcol_ok[j] = n < N;
-    const int64_t nn = bcol_ok[j] ? n : 0;
+    const int64_t nn = n < N ? n : N - 1;
     bsrc[j] = reinterpret_cast<const char *>(packed) + nn * (K / 4) + 16 * h;
     qsrc[j] = q + nn * G;
   }
@@ -97,66 +142,33 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
 
-  uint4 areg[4];
-  uint4 breg[2];
-  int qreg[2];
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  // ring of kDepth groups of global loads in flight; slot d holds group g with
+  // g % kDepth == d.  Prefetches past the last group re-read group G-1 (valid
+  // memory, discarded) so that the steady-state loop has no branches.
+  GemmStage ring[kDepth];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) areg[i] = arow_ok[i] ? *reinterpret_cast<const uint4 *>(asrc[i]) : z4;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    breg[j] = bcol_ok[j] ? *reinterpret_cast<const uint4 *>(bsrc[j]) : z4;
-    qreg[j] = bcol_ok[j] ? (int)qsrc[j][0] : 0;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(&sA[0][adst[i]]) = areg[i];
+  for (int d = 0; d < kDepth; ++d) load_stage(ring[d], min(d, G - 1), asrc, bsrc, qsrc);
+  stage_to_lds(&sA[0][0], ring[0], adst);
   __syncthreads();
 
-  for (int g = 0; g < G; ++g) {
-    const int cur = g & 1;
-    const bool more = g + 1 < G;
-    // prefetch the next group (the last iteration re-reads the current one)
-    const int gn = more ? g + 1 : g;
-    uint4 anx[4], bnx[2];
-    int qnx[2];
-    {
-      const int64_t koff = int64_t(gn) * kGroup;
+  const int full = G / kDepth * kDepth;
+  for (int g0 = 0; g0 < full; g0 += kDepth) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        anx[i] = arow_ok[i] ? *reinterpret_cast<const uint4 *>(asrc[i] + koff) : z4;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bnx[j] = bcol_ok[j] ? *reinterpret_cast<const uint4 *>(bsrc[j] + 32 * int64_t(gn)) : z4;
-        qnx[j] = bcol_ok[j] ? (int)qsrc[j][gn] : 0;
-      }
+    for (int d = 0; d < kDepth; ++d) {
+      const int g = g0 + d;
+      gemm_group(ring[d], &sA[d & 1][0], l32, h, acc);
+      load_stage(ring[d], min(g + kDepth, G - 1), asrc, bsrc, qsrc);
+      stage_to_lds(&sA[(d + 1) & 1][0], ring[(d + 1) % kDepth], adst);
+      __syncthreads();
     }
-
-    const uint32_t tab0 = perm_table(qreg[0]), tab1 = perm_table(qreg[1]);
-    const int8_t *abase = &sA[cur][l32 * kAStride + 64 * h];
+  }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint32_t w0 = s == 0 ? breg[0].x : s == 1 ? breg[0].y : s == 2 ? breg[0].z : breg[0].w;
-      const uint32_t w1 = s == 0 ? breg[1].x : s == 1 ? breg[1].y : s == 2 ? breg[1].z : breg[1].w;
-      const v4i bf0 = expand_word(w0, tab0);
-      const v4i bf1 = expand_word(w1, tab1);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const v4i af = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + 16 * s);
-        acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mt][1], 0, 0, 0);
-      }
+  for (int d = 0; d < kDepth - 1; ++d) {
+    if (full + d < G) {
+      gemm_group(ring[d], &sA[d & 1][0], l32, h, acc);
+      stage_to_lds(&sA[(d + 1) & 1][0], ring[(d + 1) % kDepth], adst);
+      __syncthreads();
     }
-
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(&sA[cur ^ 1][adst[i]]) = anx[i];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        breg[j] = bnx[j];
-        qreg[j] = qnx[j];
-      }
-    }
-    __syncthreads();
   }
 
   // epilogue: lane holds column l32 of each 32x32 tile, rows 8*(r/4) + 4*h + r%4
@@ -192,6 +204,7 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
                        int y_dtype, int32_t *acc_out, void * /*workspace*/, hipStream_t stream) {
   const int64_t gx = (N + kBN - 1) / kBN, gy = (M + kBM - 1) / kBM;
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(gx), unsigned(gy)), dim3(kThreads), 0, stream,
                      xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype, acc_out);
   set_last_kernel("gemm_i8_mfma32_128x256");

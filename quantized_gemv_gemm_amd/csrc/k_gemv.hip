@@ -93,68 +93,94 @@ __device__ __forceinline__ v4i unpack_x64(uint32_t w) {
   return r;
 }
 
+// A operand row r holds token 4*(r%4) + r/4, so D row 4q+i (lane quarter q,
+// accumulator i) holds token 4i + q: for b <= 4 every token sits in i = 0 and the
+// epilogue only touches the first ceil(b/4) accumulators.
+__device__ __forceinline__ int token_of_arow(int r) { return 4 * (r & 3) + (r >> 2); }
+
 template <int RB>
-struct GemvFrag {
-  v4i ah[2], al[2];  // activation limbs for the two 64-k halves of the group
+struct GemvSlot {
+  v4i ah[2], al[2];  // activation limbs of the group's two 64-k halves
   uint2 w[RB];       // packed words 2q, 2q+1 of the group, per row block
   uint32_t s[RB];    // fp16 scale bits
 };
 
+// Loads are unconditional: lanes whose token slot or row is out of range read a
+// valid clamped address instead, and their results are never stored.  Keeping
+// the loop free of divergent branches lets the compiler count outstanding loads
+// exactly, so four groups stay in flight.
 template <int RB>
-__device__ __forceinline__ void gemv_load(GemvFrag<RB> &f, int g, bool tok_ok,
-                                          const int8_t *ah, const int8_t *al,
-                                          const char *const (&wrow)[RB],
-                                          const uint16_t *const (&srow)[RB],
-                                          const bool (&row_ok)[RB]) {
-  const v4i z = {0, 0, 0, 0};
-  if (tok_ok) {
-    const v4i *ph = reinterpret_cast<const v4i *>(ah + 128 * int64_t(g));
-    const v4i *pl = reinterpret_cast<const v4i *>(al + 128 * int64_t(g));
-    f.ah[0] = ph[0];
-    f.ah[1] = ph[1];
-    f.al[0] = pl[0];
-    f.al[1] = pl[1];
-  } else {
-    f.ah[0] = f.ah[1] = f.al[0] = f.al[1] = z;
-  }
+__device__ __forceinline__ void gemv_load(GemvSlot<RB> &f, int g, const int8_t *ah,
+                                          const int8_t *al, const char *const (&wrow)[RB],
+                                          const uint16_t *const (&srow)[RB]) {
+  const v4i *ph = reinterpret_cast<const v4i *>(ah + 128 * int64_t(g));
+  const v4i *pl = reinterpret_cast<const v4i *>(al + 128 * int64_t(g));
+  f.ah[0] = ph[0];
+  f.ah[1] = ph[1];
+  f.al[0] = pl[0];
+  f.al[1] = pl[1];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if (row_ok[rb]) {
-      f.w[rb] = *reinterpret_cast<const uint2 *>(wrow[rb] + 32 * int64_t(g));
-      f.s[rb] = srow[rb][g];
-    } else {
-      f.w[rb] = make_uint2(0u, 0u);
-      f.s[rb] = 0u;
-    }
+    f.w[rb] = *reinterpret_cast<const uint2 *>(wrow[rb] + 32 * int64_t(g));
+    f.s[rb] = srow[rb][g];
   }
 }
 
-template <int RB, int W>
-__global__ __launch_bounds__(64 * W) void gemv_i8x2_kernel(
+template <int RB, int NT>
+__device__ __forceinline__ void gemv_compute(const GemvSlot<RB> &f, bool live, float (&acc)[RB][4]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const v4i z = {0, 0, 0, 0};
+    const v4i b0 = unpack_x64(f.w[rb].x);
+    const v4i b1 = unpack_x64(f.w[rb].y);
+    v4i dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.ah[0], b0, z, 0, 0, 0);
+    v4i dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.al[0], b0, z, 0, 0, 0);
+    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.ah[1], b1, dh, 0, 0, 0);
+    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.al[1], b1, dl, 0, 0, 0);
+    const float s = live ? half_bits_to_float((uint16_t)f.s[rb]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[rb][i] = fmaf(s, (float)(dh[i] * 256 + dl[i]), acc[rb][i]);
+  }
+}
+
+// wave cap per workgroup: larger row tiles need more registers per wave
+template <int RB>
+struct GemvWaveCap {
+  static constexpr int value = RB == 1 ? 16 : RB == 2 ? 12 : 8;
+};
+
+// One workgroup: 16*RB rows, all of K.  Its waves (blockDim.x / 64 of them) take
+// contiguous runs of 4-group chunks (one 128-byte line per row), keep the four
+// groups of a chunk in flight while the previous chunk is consumed, and reduce
+// through LDS at the end.  NT = ceil(b / 4).
+template <int RB, int NT>
+__global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_i8x2_kernel(
     const int8_t *__restrict__ xhi, const int8_t *__restrict__ xlo,
     const float *__restrict__ sigma, int b, int64_t K, int64_t N,
     const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales, void *__restrict__ y,
     int y_dtype) {
-  __shared__ float red[(W > 1 ? W - 1 : 1) * RB * 4 * 64];
+  extern __shared__ float red[];  // (W - 1) * RB * NT * 64 floats
+  const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;  // D column (weight row in block) and A row (token slot)
-  const int qd = lane >> 4;   // lane group: k quarter for A/B, token quad for D
+  const int col = lane & 15;  // B/D column = weight row in the block; A row = token slot
+  const int qd = lane >> 4;   // lane quarter: k quarter for A/B, token for D
   const int G = int(K / kGroup);
-  const int g0 = (G * wave) / W, g1 = (G * (wave + 1)) / W;
+  const int nchunk = (G + 3) >> 2;
+  const int c_begin = (nchunk * wave) / W;
+  const int c_end = (nchunk * (wave + 1)) / W;
   const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
 
-  const bool tok_ok = col < b;
-  const int8_t *ah = xhi + int64_t(col) * K + 32 * qd;
-  const int8_t *al = xlo + int64_t(col) * K + 32 * qd;
+  const int tok = token_of_arow(col);
+  const int tok_ld = tok < b ? tok : b - 1;
+  const int8_t *ah = xhi + int64_t(tok_ld) * K + 32 * qd;
+  const int8_t *al = xlo + int64_t(tok_ld) * K + 32 * qd;
   const char *wrow[RB];
   const uint16_t *srow[RB];
-  bool row_ok[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int64_t n = n0 + 16 * rb + col;
-    row_ok[rb] = n < N;
-    const int64_t nn = row_ok[rb] ? n : 0;
+    const int64_t nn = n < N ? n : N - 1;
     wrow[rb] = reinterpret_cast<const char *>(packed) + nn * (K / 4) + 8 * qd;
     srow[rb] = scales + nn * G;
   }
@@ -165,55 +191,48 @@ __global__ __launch_bounds__(64 * W) void gemv_i8x2_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[rb][i] = 0.0f;
 
-  if (g0 < g1) {
-    GemvFrag<RB> cur, nxt;
-    gemv_load<RB>(cur, g0, tok_ok, ah, al, wrow, srow, row_ok);
-    for (int g = g0; g < g1; ++g) {
-      if (g + 1 < g1) gemv_load<RB>(nxt, g + 1, tok_ok, ah, al, wrow, srow, row_ok);
+  if (c_begin < c_end) {
+    // slot j holds group 4c + j of the chunk c in flight; groups past G (only in a
+    // last, partial chunk) re-read group G-1 and are given scale 0
+    GemvSlot<RB> sl[4];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const v4i z = {0, 0, 0, 0};
-        const v4i b0 = unpack_x64(cur.w[rb].x);
-        const v4i b1 = unpack_x64(cur.w[rb].y);
-        v4i dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.ah[0], b0, z, 0, 0, 0);
-        v4i dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.al[0], b0, z, 0, 0, 0);
-        dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.ah[1], b1, dh, 0, 0, 0);
-        dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(cur.al[1], b1, dl, 0, 0, 0);
-        const float s = half_bits_to_float((uint16_t)cur.s[rb]);
+    for (int j = 0; j < 4; ++j) gemv_load<RB>(sl[j], min(4 * c_begin + j, G - 1), ah, al, wrow, srow);
+    for (int c = c_begin; c < c_end - 1; ++c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][i] = fmaf(s, (float)(dh[i] * 256 + dl[i]), acc[rb][i]);
+      for (int j = 0; j < 4; ++j) {
+        gemv_compute<RB, NT>(sl[j], true, acc);
+        gemv_load<RB>(sl[j], min(4 * (c + 1) + j, G - 1), ah, al, wrow, srow);
       }
-      if (g + 1 < g1) cur = nxt;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gemv_compute<RB, NT>(sl[j], 4 * (c_end - 1) + j < G, acc);
   }
 
-  // reduce the W partial sums through LDS; wave 0 finishes
   if (W > 1) {
     if (wave > 0) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[(((wave - 1) * RB + rb) * 4 + i) * 64 + lane] = acc[rb][i];
+        for (int i = 0; i < NT; ++i) red[(((wave - 1) * RB + rb) * NT + i) * 64 + lane] = acc[rb][i];
     }
     __syncthreads();
     if (wave > 0) return;
-#pragma unroll
     for (int w = 1; w < W; ++w)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][i] += red[(((w - 1) * RB + rb) * 4 + i) * 64 + lane];
+        for (int i = 0; i < NT; ++i) acc[rb][i] += red[(((w - 1) * RB + rb) * NT + i) * 64 + lane];
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = 4 * qd + i;  // D row = token slot
+  for (int i = 0; i < NT; ++i) {
+    const int t = 4 * i + qd;  // token held by D row 4*qd + i
     if (t >= b) continue;
     const float sc = sigma[t] * (1.0f / 64.0f);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (!row_ok[rb]) continue;
       const int64_t n = n0 + 16 * rb + col;
+      if (n >= N) continue;
       const float v = acc[rb][i] * sc;
       if (y_dtype == TL_F32)
         reinterpret_cast<float *>(y)[int64_t(t) * N + n] = v;
@@ -225,15 +244,47 @@ __global__ __launch_bounds__(64 * W) void gemv_i8x2_kernel(
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-template <int RB, int W>
-hipError_t launch_main(const int8_t *xhi, const int8_t *xlo, const float *sigma, int64_t b,
-                       int64_t K, int64_t N, const uint32_t *packed, const uint16_t *scales,
-                       void *y, int y_dtype, hipStream_t stream, const char *name) {
+template <int RB, int NT>
+hipError_t launch_main_rb_nt(const int8_t *xhi, const int8_t *xlo, const float *sigma, int64_t b,
+                             int64_t K, int64_t N, const uint32_t *packed, const uint16_t *scales,
+                             void *y, int y_dtype, int waves, hipStream_t stream) {
   const int64_t grid = (N + 16 * RB - 1) / (16 * RB);
-  hipLaunchKernelGGL((gemv_i8x2_kernel<RB, W>), dim3(unsigned(grid)), dim3(64 * W), 0, stream,
-                     xhi, xlo, sigma, int(b), K, N, packed, scales, y, y_dtype);
-  set_last_kernel(name);
+  const size_t lds = size_t(waves > 1 ? waves - 1 : 1) * RB * NT * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemv_i8x2_kernel<RB, NT>), dim3(unsigned(grid)), dim3(64 * waves), lds,
+                     stream, xhi, xlo, sigma, int(b), K, N, packed, scales, y, y_dtype);
   return hipGetLastError();
+}
+
+template <int RB>
+hipError_t launch_main_rb(const int8_t *xhi, const int8_t *xlo, const float *sigma, int64_t b,
+                          int64_t K, int64_t N, const uint32_t *packed, const uint16_t *scales,
+                          void *y, int y_dtype, int waves, hipStream_t stream) {
+  switch ((b + 3) / 4) {
+    case 1: return launch_main_rb_nt<RB, 1>(xhi, xlo, sigma, b, K, N, packed, scales, y, y_dtype, waves, stream);
+    case 2: return launch_main_rb_nt<RB, 2>(xhi, xlo, sigma, b, K, N, packed, scales, y, y_dtype, waves, stream);
+    case 3: return launch_main_rb_nt<RB, 3>(xhi, xlo, sigma, b, K, N, packed, scales, y, y_dtype, waves, stream);
+    default: return launch_main_rb_nt<RB, 4>(xhi, xlo, sigma, b, K, N, packed, scales, y, y_dtype, waves, stream);
+  }
+}
+
+struct GemvVariant {
+  int rb, waves;
+  const char *name;
+};
+
+// Rows per workgroup (16*rb) and waves per workgroup for a problem size.  Each
+// wave should own at least one 4-group chunk; row blocks per workgroup trade
+// CU coverage (more, smaller workgroups) against activation re-reads (each
+// workgroup reads all of the b x K activations).
+GemvVariant choose_gemv(int64_t b, int64_t K, int64_t N) {
+  const int64_t G = K / kGroup, nchunk = (G + 3) / 4;
+  int rb = 1;
+  if (b > 4 && N >= 64 * 256) rb = 4;
+  else if (b > 4 && N >= 32 * 256) rb = 2;
+  const int cap = rb == 1 ? GemvWaveCap<1>::value : rb == 2 ? GemvWaveCap<2>::value : GemvWaveCap<4>::value;
+  const int waves = int(nchunk < cap ? nchunk : cap);
+  static const char *names[3] = {"gemv_i8x2_rb1", "gemv_i8x2_rb2", "gemv_i8x2_rb4"};
+  return {rb, waves, names[rb == 1 ? 0 : rb == 2 ? 1 : 2]};
 }
 
 }  // namespace
@@ -259,6 +310,7 @@ GemvWs carve(void *workspace, int64_t b, int64_t K) {
 hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
                                hipStream_t stream) {
   const GemvWs w = carve(workspace, b, K);
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(gemv_prep_kernel, dim3(unsigned(b)), dim3(kPrepThreads), 0, stream, xr, K,
                      w.xhi, w.xlo, w.sigma);
   set_last_kernel("gemv_prep_limbs");
@@ -269,14 +321,17 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
                             const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
                             hipStream_t stream) {
   const GemvWs w = carve(const_cast<void *>(workspace), b, K);
-  if (N >= 64 * 128)
-    return launch_main<4, 8>(w.xhi, w.xlo, w.sigma, b, K, N, packed, scales, y, y_dtype, stream,
-                             "gemv_i8x2_rb4_w8");
-  if (N >= 32 * 128)
-    return launch_main<2, 8>(w.xhi, w.xlo, w.sigma, b, K, N, packed, scales, y, y_dtype, stream,
-                             "gemv_i8x2_rb2_w8");
-  return launch_main<1, 8>(w.xhi, w.xlo, w.sigma, b, K, N, packed, scales, y, y_dtype, stream,
-                           "gemv_i8x2_rb1_w8");
+  const GemvVariant v = choose_gemv(b, K, N);
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
+  hipError_t e;
+  if (v.rb == 4)
+    e = launch_main_rb<4>(w.xhi, w.xlo, w.sigma, b, K, N, packed, scales, y, y_dtype, v.waves, stream);
+  else if (v.rb == 2)
+    e = launch_main_rb<2>(w.xhi, w.xlo, w.sigma, b, K, N, packed, scales, y, y_dtype, v.waves, stream);
+  else
+    e = launch_main_rb<1>(w.xhi, w.xlo, w.sigma, b, K, N, packed, scales, y, y_dtype, v.waves, stream);
+  set_last_kernel(v.name);
+  return e;
 }
 
 }  // namespace tl

@@ -103,6 +103,7 @@ hipError_t launch_hadamard(const uint16_t *x, int64_t T, int64_t K, const int8_t
   const int nblk = int(K / kHBlock);
   const int64_t grid = T * nblk;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(hadamard_blk_kernel, dim3(unsigned(grid)), dim3(64), 0, stream, x, signs, xr,
                      K, nblk);
   set_last_kernel("hadamard_blk_f64x16");

@@ -75,6 +75,7 @@ hipError_t launch_pack(const int8_t *codes, const uint16_t *scales, int64_t N, i
                        uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
                        hipStream_t stream) {
   if (N > 0x7FFFFFFF) return hipErrorInvalidValue;
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(pack_rows_kernel, dim3(unsigned(N)), dim3(kThreads), 0, stream, codes, scales,
                      K, packed, q, row_scale, invalid_count);
   set_last_kernel("pack_rows");

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float *__rest
 hipError_t launch_quant(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
                         hipStream_t stream) {
   if (T > 0x7FFFFFFF) return hipErrorInvalidValue;
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(quant_act_kernel, dim3(unsigned(T)), dim3(kThreads), 0, stream, xr, K, xq,
                      tok_scale);
   set_last_kernel("quant_act_int8");

@@ -8,6 +8,7 @@
 
 namespace tl {
 static thread_local const char *g_last_kernel = "";
+static thread_local const char *g_last_error = "";
 void set_last_kernel(const char *name) { g_last_kernel = name; }
 }  // namespace tl
 
@@ -37,7 +38,11 @@ bool any_alias(const Span *in, int nin, const Span *out, int nout) {
   return false;
 }
 
-int from_hip(hipError_t e) { return e == hipSuccess ? TL_OK : TL_ERR_LAUNCH; }
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return TL_OK;
+  tl::g_last_error = hipGetErrorString(e);
+  return TL_ERR_LAUNCH;
+}
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;  // rows, tokens and K stay below 2^31
 
@@ -63,6 +68,8 @@ const char *tl_status_string(int s) {
 }
 
 const char *tl_last_kernel_name(void) { return tl::g_last_kernel; }
+
+const char *tl_last_error_detail(void) { return tl::g_last_error; }
 
 int tl_pack_weights(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                     uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
@@ -160,7 +167,7 @@ int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint
   if (any_alias(in, 3, out, 2)) return TL_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = tl::launch_gemv_prepare(xr, b, K, workspace, st);
-  if (e != hipSuccess) return TL_ERR_LAUNCH;
+  if (e != hipSuccess) return from_hip(e);
   return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype, st));
 }
 
