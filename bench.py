@@ -1,10 +1,12 @@
 """Benchmark of the ternary linear layer on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  decode  (qkv layer, K=5120 -> N=10240) for b = 1, 4, 8 and 16 tokens:
-          block rotation -> GEMV activation prep -> GEMV weight stream;
-  prefill (512-token chunk) for gate_up (5120 -> 34816) and down (17408 -> 5120):
-          block rotation -> per-token int8 quantisation -> int8 GEMM + rescale.
+  decode  for b = 1, 4, 8 and 16 tokens: block rotation -> GEMV activation prep
+          -> the GEMV weight stream of DEC_LAYERS qkv-shaped layers
+          (K=5120 -> N=10240, each a different weight copy);
+  prefill (512-token chunk): for gate_up (5120 -> 34816) and down (17408 -> 5120),
+          block rotation -> per-token int8 quantisation -> int8 GEMM + rescale of
+          PRE_LAYERS layers each.
 Weights are packed once (load time, not timed) and cloned into rotating copies
 (>= 1 GiB per layer type) so that successive launches read weights that are not
 resident in the 256 MB Infinity Cache.
@@ -13,7 +15,10 @@ Reported: decode GEMV GB/s (algorithmic bytes / kernel time, aggregated over the
 four batch sizes) as `value`, its fraction of the 8 TB/s HBM peak, prefill int8
 TOP/s against the 5.0 POP/s dense int8 peak, and the CPU oracle timed on a
 bounded sample.  Kernel durations come from HIP events recorded on the stream
-the kernels run on (torch's current stream) around each launch.
+the kernels run on (torch's current stream) around each back-to-back run of
+GEMV (or GEMM) launches inside the timed steps, divided by the launch count;
+bracketing runs rather than single launches keeps the event overhead out of the
+per-launch figure, which then matches the rocprofv3 kernel durations.
 """
 from __future__ import annotations
 
@@ -36,6 +41,8 @@ ROTATE_BYTES = 2 ** 30
 
 DECODE_BS = (1, 4, 8, 16)
 PREFILL_M = 512
+DEC_LAYERS = 8     # qkv-shaped layers per decode pass (distinct weight copies)
+PRE_LAYERS = 2     # layers of each MLP type per prefill pass
 
 
 def gemv_bytes(b, K, N):
@@ -119,33 +126,39 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    kernel_names = {}
+
     def step(rec):
-        """One pass of the hot path; appends (kind, key, start, end) events when rec is a list."""
+        """One pass of the hot path; appends (kind, key, n_launches, start, end) when rec is a list."""
         for b in DECODE_BS:
-            packed, scales, _, _ = qkv[rot["qkv"] % len(qkv)]
-            rot["qkv"] += 1
             tl.hadamard_blk(x_dec[b], out=xr_dec[b])
             tl.gemv_prepare(xr_dec[b], ws_dec[b])
             if rec is not None:
                 e0, e1 = ev(), ev()
                 e0.record(stream)
-            tl.gemv_prepared(ws_dec[b], b, Kq, packed, scales, y_dec[b])
+            for _ in range(DEC_LAYERS):
+                packed, scales, _, _ = qkv[rot["qkv"] % len(qkv)]
+                rot["qkv"] += 1
+                tl.gemv_prepared(ws_dec[b], b, Kq, packed, scales, y_dec[b])
+            kernel_names[("gemv", b)] = tl.last_kernel_name()
             if rec is not None:
                 e1.record(stream)
-                rec.append(("gemv", b, e0, e1))
+                rec.append(("gemv", b, DEC_LAYERS, e0, e1))
         for name in ("gate_up", "down"):
             P = pre[name]
-            packed, _, q, rs = P["copies"][rot[name] % len(P["copies"])]
-            rot[name] += 1
             tl.hadamard_blk(P["x"], out=P["xr"])
             tl.quant_act_int8(P["xr"], P["xq"], P["sx"])
             if rec is not None:
                 e0, e1 = ev(), ev()
                 e0.record(stream)
-            tl.gemm_int8_rescale(P["xq"], P["sx"], packed, q, rs, out=P["y"])
+            for _ in range(PRE_LAYERS):
+                packed, _, q, rs = P["copies"][rot[name] % len(P["copies"])]
+                rot[name] += 1
+                tl.gemm_int8_rescale(P["xq"], P["sx"], packed, q, rs, out=P["y"])
+            kernel_names[("gemm", name)] = tl.last_kernel_name()
             if rec is not None:
                 e1.record(stream)
-                rec.append(("gemm", name, e0, e1))
+                rec.append(("gemm", name, PRE_LAYERS, e0, e1))
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -165,8 +178,8 @@ def main():
 
     gemv_ms = {b: [] for b in DECODE_BS}
     gemm_ms = {"gate_up": [], "down": []}
-    for kind, key, e0, e1 in rec:
-        (gemv_ms if kind == "gemv" else gemm_ms)[key].append(e0.elapsed_time(e1))
+    for kind, key, n, e0, e1 in rec:
+        (gemv_ms if kind == "gemv" else gemm_ms)[key].append(e0.elapsed_time(e1) / n)
 
     by_b = {}
     tot_bytes = tot_s = 0.0
@@ -174,7 +187,8 @@ def main():
         t = float(np.mean(gemv_ms[b])) * 1e-3
         nbytes = gemv_bytes(b, Kq, Nq)
         by_b[str(b)] = {"us": round(t * 1e6, 3), "GBps": round(nbytes / t / 1e9, 1),
-                        "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+                        "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "kernel": kernel_names[("gemv", b)],
+                        "bytes": nbytes}
         tot_bytes += nbytes
         tot_s += t
     dec_gbs = tot_bytes / tot_s / 1e9
@@ -185,7 +199,7 @@ def main():
         t = float(np.mean(gemm_ms[name])) * 1e-3
         ops = 2.0 * PREFILL_M * pre[name]["K"] * pre[name]["N"]
         pre_out[name] = {"us": round(t * 1e6, 2), "TOPs": round(ops / t / 1e12, 1),
-                         "frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4)}
+                         "frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4), "kernel": kernel_names[("gemm", name)]}
         ops_tot += ops
         t_tot += t
     pre_tops = ops_tot / t_tot / 1e12
@@ -208,8 +222,9 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "ternary linear layer: decode qkv K=5120 N=10240 at b=1,4,8,16 "
-                               "+ prefill M=512 gate_up 5120->34816 and down 17408->5120",
+        "config": {"workload": f"ternary linear layer: decode qkv K=5120 N=10240 at b=1,4,8,16 "
+                               f"({DEC_LAYERS} layers per pass) + prefill M=512 gate_up 5120->34816 and "
+                               f"down 17408->5120 ({PRE_LAYERS} layers each)",
                    "decode_b": list(DECODE_BS), "prefill_tokens": PREFILL_M,
                    "rotating_weight_bytes": ROTATE_BYTES},
         "decode_gemv_by_b": by_b,
@@ -217,16 +232,12 @@ def main():
         "prefill_gemm": pre_out,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": tl_kernel_name_for_gemv()},
+                     "kernel": "GEMV weight stream (" + ", ".join(sorted({v["kernel"] for v in by_b.values()})) + ")"},
         "roofline_prefill": {"bound": "mfma", "achieved": round(pre_tops, 1), "peak": INT8_PEAK_TOPS,
                              "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-
-
-def tl_kernel_name_for_gemv():
-    return "gemv_i8x2_rb4_w8"
 
 
 def cpu_baseline(seconds):

@@ -33,13 +33,22 @@
  *   - Calls are thread-safe; concurrent calls on different streams are
  *     independent (each uses only its own arguments and workspace).
  *
- * Packed weight layout (ABI version 1; the page gives no layout, this one is ours)
- *   packed is uint32 [N, K/16].  Word w of row n holds the codes of
- *   k = 16 w + j, j = 0..15.  Code j occupies bits 8*(j mod 4) + 2*(j div 4) and
- *   the bit above it, so byte b of the word holds codes j = b, b+4, b+8, b+12 in
- *   its bit pairs 0..3.  A field is the code's two's-complement low two bits:
- *   0 -> 00, +1 -> 01, -1 -> 11 (10 is never written).  With this order,
- *   ((w >> 2r) & 0x03030303) holds codes 4r..4r+3 in bytes 0..3, in k order.
+ * Packed weight layout (ABI version 2; the page gives no layout, this one is ours)
+ *   Codes are stored two bits each in uint32 words.  Within a word, code j
+ *   (j = 0..15, for 16 consecutive k) occupies bits 8*(j mod 4) + 2*(j div 4) and
+ *   the bit above it, so ((w >> 2r) & 0x03030303) holds codes 4r..4r+3 in bytes
+ *   0..3, in k order.  A field is the code's two's-complement low two bits:
+ *   0 -> 00, +1 -> 01, -1 -> 11 (10 is never written).
+ *   Words are grouped in 1024-byte tiles that match the lanes of a 64-wide
+ *   wavefront: rows are taken in blocks of 16 and K in pairs of 128-groups,
+ *   NB = ceil(N/16) row blocks, GP = ceil(K/256) group pairs (a last partial
+ *   block or pair is padded with zero codes).  Tile (rb, p) starts at word
+ *   256*(rb*GP + p).  Its word 4*l + 2*gi + m (l = 0..63, gi, m in {0, 1}) holds
+ *   the codes k = 128*(2p + gi) + 16*(2*(l/16) + m) + j, j = 0..15, of row
+ *   n = 16*rb + (l mod 16).  Lane l of a wavefront reading 16 bytes at
+ *   4*l words thus gets, for both groups of the pair, the two words an
+ *   int8 16x16x64 matrix instruction needs from it.  tl_packed_bytes(N, K)
+ *   gives the size.
  */
 #ifndef TL_H
 #define TL_H
@@ -51,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TL_ABI_VERSION 1
+#define TL_ABI_VERSION 2
 
 /* status codes returned by every call */
 #define TL_OK 0
@@ -88,7 +97,8 @@ const char *tl_last_error_detail(void);
  *   [P1] "4. 効いた高速化" (q[n,g] = round(127 s[n,g] / smax[n])).
  * in  codes      int8   [N, K]     values in {-1, 0, +1}
  * in  scales     fp16   [N, K/128] (raw IEEE half bits), finite
- * out packed     uint32 [N, K/16]  layout above
+ * out packed     uint32, tl_packed_bytes(N, K) bytes, layout above (padding
+ *                included and written)
  * out q          int8   [N, K/128] q = RNE( fl32(fl32(127*s) / smax) ),
  *                                  smax[n] = max_g |s[n,g]|; |q| <= 127
  * out row_scale  f32    [N]        fl32(smax / 127)
@@ -97,6 +107,7 @@ const char *tl_last_error_detail(void);
  * A row whose scales are all zero gets q = 0 and row_scale = 0.
  * Requires K > 0, K % 128 == 0.
  */
+size_t tl_packed_bytes(int64_t N, int64_t K);
 int tl_pack_weights(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                     uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
                     void *stream);
@@ -121,7 +132,7 @@ int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs
  * tl_gemv_ternary -- decode GEMV, y = W xr for 1..16 tokens.
  *   [P1] "前提" (y = W (H_blk x), W = code * group scale).
  * in  xr      f32    [b, K]      rotated activations (tl_hadamard_blk output)
- * in  packed  uint32 [N, K/16]   from tl_pack_weights
+ * in  packed  uint32 tiles      from tl_pack_weights (tl_packed_bytes(N, K) bytes)
  * in  scales  fp16   [N, K/128]
  * out y       [b, N] of y_dtype: y[t,n] = sum_g s[n,g] sum_{k in g} code[n,k] xr[t,k]
  * workspace   device scratch of at least tl_gemv_workspace_size(b, K, N) bytes,
@@ -174,7 +185,7 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
  *   then a per-row and per-token rescale).
  * in  xq         int8   [M, K]     from tl_quant_act_int8
  * in  tok_scale  f32    [M]
- * in  packed     uint32 [N, K/16]  from tl_pack_weights
+ * in  packed     uint32 tiles     from tl_pack_weights
  * in  q          int8   [N, K/128] from tl_pack_weights
  * in  row_scale  f32    [N]        from tl_pack_weights
  * out y          [M, N] of y_dtype: y = fl32( fl32(acc) * row_scale[n] ) * tok_scale[m]

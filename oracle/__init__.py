@@ -12,7 +12,7 @@ as [P1] with its section headings.
 Every function is the plain definition, written with numpy in binary64 unless a
 step is an integer decision; there is no blocking, fusion or reordering beyond
 what the definition states.  Readings of points the page leaves open are marked
-READING and collected in DESIGN.md.
+READING; each reading is stated where it is used.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, textbook identities, exact rational arithmetic and brute force.
@@ -23,6 +23,9 @@ from .ternary import (  # noqa: F401
     sylvester_hadamard,
     rotate_exact,
     rotate_f32,
+    encode_words,
+    decode_words,
+    packed_size_words,
     pack_codes,
     unpack_codes,
     decompose_scales,

@@ -77,17 +77,19 @@ def rotate_f32(x: np.ndarray, signs: np.ndarray | None = None) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # packed 2-bit codes  ([P1] "前提": 2-bit representation of {-1, 0, +1})
 # ---------------------------------------------------------------------------
-# The page does not give the bit layout; this one is ours (include/tl.h):
-#   word w of row n holds codes k = 16 w + j, j = 0..15;
-#   code j sits in byte (j mod 4), bit pair (j div 4) of that byte, i.e. at bits
-#   8*(j mod 4) + 2*(j div 4) .. +1;
-#   field = two's complement low 2 bits: 0 -> 00, +1 -> 01, -1 -> 11.
+# The page does not give the bit layout; this one is ours (include/tl.h, ABI 2).
+# Word encoding: a uint32 holds 16 codes k = 16w + j; code j sits in byte
+# (j mod 4), bit pair (j div 4) of that byte, i.e. at bits 8*(j mod 4) + 2*(j div 4)
+# .. +1; field = two's complement low 2 bits: 0 -> 00, +1 -> 01, -1 -> 11.
+# Tile order: rows in blocks of 16, K in pairs of 128-groups (zero padded);
+# tile (rb, p) = 256 words at 256*(rb*GP + p); its word 4*l + 2*gi + m holds
+# codes 128*(2p+gi) + 16*(2*(l//16) + m) + j of row 16*rb + l%16.
 def _bitpos(j: np.ndarray) -> np.ndarray:
     return 8 * (j % 4) + 2 * (j // 4)
 
 
-def pack_codes(codes: np.ndarray) -> np.ndarray:
-    """codes int8 [N, K] in {-1,0,1} -> uint32 [N, K/16] (layout above)."""
+def encode_words(codes: np.ndarray) -> np.ndarray:
+    """codes int8 [N, K] in {-1,0,1} -> row-major words uint32 [N, K/16] (word encoding only)."""
     codes = np.asarray(codes)
     N, K = codes.shape
     if K % 16:
@@ -100,15 +102,54 @@ def pack_codes(codes: np.ndarray) -> np.ndarray:
     return words.astype(np.uint32)
 
 
-def unpack_codes(packed: np.ndarray, K: int) -> np.ndarray:
-    """Inverse of :func:`pack_codes` (field 10 decodes to -2, flagging a bad word)."""
-    packed = np.asarray(packed, dtype=np.uint32).astype(np.int64)
-    N = packed.shape[0]
-    out = np.empty((N, K // 16, 16), dtype=np.int8)
+def decode_words(words: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`encode_words` (field 10 decodes to -2, flagging a bad word)."""
+    w = np.asarray(words, dtype=np.uint32).astype(np.int64)
+    N, nw = w.shape
+    out = np.empty((N, nw, 16), dtype=np.int8)
     for j in range(16):
-        f = (packed >> int(_bitpos(np.array(j)))) & 3
+        f = (w >> int(_bitpos(np.array(j)))) & 3
         out[:, :, j] = np.where(f >= 2, f - 4, f)
-    return out.reshape(N, K)
+    return out.reshape(N, nw * 16)
+
+
+def packed_size_words(N: int, K: int) -> int:
+    NB, GP = -(-N // 16), -(-K // 256)
+    return NB * GP * 256
+
+
+def _tile_index(N: int, K: int):
+    """For every (padded row, padded word column) its index in the tiled array."""
+    NB, GP = -(-N // 16), -(-K // 256)
+    n = np.arange(NB * 16)[:, None]
+    wc = np.arange(GP * 16)[None, :]          # word column: 16 words per group pair
+    rb, nl = n // 16, n % 16
+    g, w = wc // 8, wc % 8                     # group, word within group
+    p, gi = g // 2, g % 2
+    q, m = w // 2, w % 2
+    lane = 16 * q + nl
+    return 256 * (rb * GP + p) + 4 * lane + 2 * gi + m
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """codes int8 [N, K] -> the tiled packed array, uint32 [packed_size_words(N, K)]."""
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    NB, GP = -(-N // 16), -(-K // 256)
+    padded = np.zeros((NB * 16, GP * 256), dtype=np.int8)
+    padded[:N, :K] = codes
+    words = encode_words(padded)
+    out = np.zeros(packed_size_words(N, K), dtype=np.uint32)
+    out[_tile_index(N, K)] = words
+    return out
+
+
+def unpack_codes(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """Inverse of :func:`pack_codes`: codes [N, K] (field 10 decodes to -2)."""
+    words = np.asarray(packed, dtype=np.uint32)[_tile_index(N, K)]
+    return decode_words(words)[:N, :K]
 
 
 # ---------------------------------------------------------------------------

@@ -32,6 +32,7 @@ _SIGS = {
     "tl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tl_last_kernel_name": (ctypes.c_char_p, []),
     "tl_last_error_detail": (ctypes.c_char_p, []),
+    "tl_packed_bytes": (_c_sz, [_c_i64, _c_i64]),
     "tl_pack_weights": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "tl_hadamard_blk": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "tl_gemv_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
@@ -119,24 +120,35 @@ def _out_code(dtype):
 # ---------------------------------------------------------------------------
 # the five calls
 # ---------------------------------------------------------------------------
+def packed_words(N: int, K: int) -> int:
+    """Number of uint32 words of the packed (tiled) weights of an [N, K] layer."""
+    return int(lib().tl_packed_bytes(N, K)) // 4
+
+
+def _check_packed(packed, N, K):
+    import torch
+    _need(packed, "packed", torch.int32, 1)
+    if packed.numel() != packed_words(N, K):
+        raise ValueError(f"packed must hold {packed_words(N, K)} words for N={N}, K={K}")
+
+
 def pack_weights(codes, scales, packed=None, q=None, row_scale=None, invalid_count=None):
-    """codes int8 [N,K], scales fp16 [N,K/128] -> (packed int32 [N,K/16], q int8 [N,K/128],
-    row_scale f32 [N]).  ``packed`` holds the uint32 words (torch has no uint32 math)."""
+    """codes int8 [N,K], scales fp16 [N,K/128] -> (packed int32 [packed_words(N,K)] (the uint32
+    tile words of the layout in include/tl.h), q int8 [N,K/128], row_scale f32 [N])."""
     import torch
     _need(codes, "codes", torch.int8, 2)
     _need(scales, "scales", torch.float16, 2)
     N, K = codes.shape
     dev = codes.device
-    packed = torch.empty((N, K // 16), dtype=torch.int32, device=dev) if packed is None else packed
+    packed = torch.empty((packed_words(N, K),), dtype=torch.int32, device=dev) if packed is None else packed
     q = torch.empty((N, K // GROUP), dtype=torch.int8, device=dev) if q is None else q
     row_scale = torch.empty((N,), dtype=torch.float32, device=dev) if row_scale is None else row_scale
-    _need(packed, "packed", torch.int32, 2)
+    _check_packed(packed, N, K)
     _need(q, "q", torch.int8, 2)
     _need(row_scale, "row_scale", torch.float32, 1)
     if invalid_count is not None:
         _need(invalid_count, "invalid_count", torch.int32, 1)
-    if scales.shape != (N, K // GROUP) or packed.shape != (N, K // 16) or q.shape != (N, K // GROUP) \
-            or row_scale.shape != (N,):
+    if scales.shape != (N, K // GROUP) or q.shape != (N, K // GROUP) or row_scale.shape != (N,):
         raise ValueError("shape mismatch in pack_weights")
     _check("tl_pack_weights", lib().tl_pack_weights(
         _ptr(codes), _ptr(scales), N, K, _ptr(packed), _ptr(q), _ptr(row_scale), _ptr(invalid_count),
@@ -166,14 +178,14 @@ def gemv_workspace_size(b: int, K: int, N: int) -> int:
 
 
 def gemv_ternary(xr, packed, scales, out_dtype=None, out=None, workspace=None):
-    """xr f32 [b,K] (b <= 16), packed [N,K/16], scales fp16 [N,K/128] -> y [b,N]."""
+    """xr f32 [b,K] (b <= 16), packed tiles, scales fp16 [N,K/128] -> y [b,N]."""
     import torch
     _need(xr, "xr", torch.float32, 2)
-    _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
     b, K = xr.shape
-    N = packed.shape[0]
-    if packed.shape != (N, K // 16) or scales.shape != (N, K // GROUP):
+    N = scales.shape[0]
+    _check_packed(packed, N, K)
+    if scales.shape != (N, K // GROUP):
         raise ValueError("shape mismatch in gemv_ternary")
     if out is None:
         out = torch.empty((b, N), dtype=out_dtype or torch.bfloat16, device=xr.device)
@@ -206,10 +218,10 @@ def gemv_prepared(workspace, b, K, packed, scales, out):
     """Second stage of gemv_ternary: y [b,N] from a workspace filled by gemv_prepare(b, K)."""
     import torch
     _need(workspace, "workspace", torch.uint8, 1)
-    _need(packed, "packed", torch.int32, 2)
     _need(scales, "scales", torch.float16, 2)
-    N = packed.shape[0]
-    if packed.shape != (N, K // 16) or scales.shape != (N, K // GROUP) or out.shape != (b, N):
+    N = scales.shape[0]
+    _check_packed(packed, N, K)
+    if scales.shape != (N, K // GROUP) or out.shape != (b, N):
         raise ValueError("shape mismatch in gemv_prepared")
     code = _out_code(out.dtype)
     _need(out, "out", out.dtype, 2)
@@ -246,13 +258,12 @@ def gemm_int8_rescale(xq, tok_scale, packed, q, row_scale, out_dtype=None, out=N
     import torch
     _need(xq, "xq", torch.int8, 2)
     _need(tok_scale, "tok_scale", torch.float32, 1)
-    _need(packed, "packed", torch.int32, 2)
     _need(q, "q", torch.int8, 2)
     _need(row_scale, "row_scale", torch.float32, 1)
     M, K = xq.shape
-    N = packed.shape[0]
-    if tok_scale.shape != (M,) or packed.shape != (N, K // 16) or q.shape != (N, K // GROUP) \
-            or row_scale.shape != (N,):
+    N = q.shape[0]
+    _check_packed(packed, N, K)
+    if tok_scale.shape != (M,) or q.shape != (N, K // GROUP) or row_scale.shape != (N,):
         raise ValueError("shape mismatch in gemm_int8_rescale")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=xq.device)

@@ -10,11 +10,12 @@
 //
 // Tiling (CDNA4, v_mfma_i32_32x32x32_i8): a 256-thread workgroup computes a
 // 128 x 256 tile of y; each of its 4 waves owns 128 x 64 (4 x 2 MFMA tiles,
-// 128 int32 accumulators per lane).  The K loop steps one 128-wide scale group
-// at a time (4 MFMA k-steps).  The activation tile (128 rows x 128 bytes) is
-// staged in LDS, double buffered, and shared by the 4 waves.  Each wave loads
-// its own weight columns straight from global memory: one 16-byte load per
-// column per group gives the 4 words that feed the group's 4 k-steps.  The
+// 128 int32 accumulators per lane).  The K loop steps one pair of 128-wide scale
+// groups at a time (8 MFMA k-steps), with two pairs of loads in flight.  The
+// activation tile (128 rows x 256 bytes) is staged in LDS, double buffered, and
+// shared by the 4 waves.  Each wave loads its own weight columns straight from
+// the packed tiles: two 16-byte loads per column per pair give the 8 words that
+// feed the pair's 8 k-steps.  The
 // expansion code -> code*q is one v_perm_b32 per 4 weights: the selector bytes
 // are the 2-bit fields ((w >> 2r) & 0x03030303) and the table holds
 // {0, q, -, -q}.  The packed layout puts codes 4r..4r+3 in bytes 0..3 of that
@@ -31,18 +32,19 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 constexpr int kBM = 128;
 constexpr int kBN = 256;
 constexpr int kThreads = 256;
-constexpr int kAStride = kGroup + 16;  // LDS row pitch in bytes (padding spreads banks)
+constexpr int kPairK = 2 * kGroup;        // k per pipeline stage: one pair of groups
+constexpr int kAStride = kPairK + 16;     // LDS row pitch in bytes (padding spreads banks)
+constexpr int kDepth = 2;                 // pairs of global loads in flight per thread
 
-static_assert(kBM * kGroup == kThreads * 4 * 16, "A stage = 4 x 16 bytes per thread");
+static_assert(kBM * kPairK == kThreads * 8 * 16, "A stage = 8 x 16 bytes per thread");
 static_assert(kBN == 4 * 64, "4 waves x 64 columns");
-constexpr int kDepth = 4;  // groups of global loads in flight per thread
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 struct GemmStage {
-  v4u a[4];  // this thread's four 16-byte pieces of the 128 x 128 activation tile
-  v4u b[2];  // packed words 4h..4h+3 of the group for the lane's two weight columns
-  int q[2];  // q of those columns for the group
+  v4u a[8];     // this thread's eight 16-byte pieces of the 128 x 256 activation tile
+  v4u b[2][2];  // [N tile][lane quarter 2h, 2h+1]: tile words for both groups of the pair
+  int q[2][2];  // [N tile][group of the pair]
 };
 
 __device__ __forceinline__ uint32_t perm_table(int qv) {
@@ -52,23 +54,31 @@ __device__ __forceinline__ uint32_t perm_table(int qv) {
 
 // Loads are unconditional: rows past M and columns past N read a clamped, valid
 // address and their results are never stored.  With no divergent branches the
-// compiler can count outstanding loads exactly and keep kDepth groups in flight.
-__device__ __forceinline__ void load_stage(GemmStage &st, int g, const int8_t *const (&asrc)[4],
-                                           const char *const (&bsrc)[2],
+// compiler can count outstanding loads exactly and keep kDepth pairs in flight.
+__device__ __forceinline__ void load_stage(GemmStage &st, int p, int64_t K, int G, int GP,
+                                           const int8_t *const (&arow)[8], const int (&acol)[8],
+                                           const uint32_t *const (&bsrc)[2],
                                            const int8_t *const (&qsrc)[2]) {
-  const int64_t koff = int64_t(g) * kGroup;
+  const int64_t koff = int64_t(p) * kPairK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.a[i] = *reinterpret_cast<const v4u *>(asrc[i] + koff);
+  for (int i = 0; i < 8; ++i) {
+    // the padded half of a last odd pair re-reads the row's last group (zero weights)
+    const int64_t o = koff + acol[i] < K ? koff + acol[i] : koff + acol[i] - kGroup;
+    st.a[i] = *reinterpret_cast<const v4u *>(arow[i] + o);
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    st.b[j] = *reinterpret_cast<const v4u *>(bsrc[j] + 32 * int64_t(g));
-    st.q[j] = (int)qsrc[j][g];
+    const uint32_t *t = bsrc[j] + 256 * int64_t(p);
+    st.b[j][0] = *reinterpret_cast<const v4u *>(t);
+    st.b[j][1] = *reinterpret_cast<const v4u *>(t + 64);
+    st.q[j][0] = (int)qsrc[j][2 * p];
+    st.q[j][1] = 2 * p + 1 < G ? (int)qsrc[j][2 * p + 1] : 0;
   }
 }
 
-__device__ __forceinline__ void stage_to_lds(int8_t *buf, const GemmStage &st, const int (&adst)[4]) {
+__device__ __forceinline__ void stage_to_lds(int8_t *buf, const GemmStage &st, const int (&adst)[8]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u *>(buf + adst[i]) = st.a[i];
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u *>(buf + adst[i]) = st.a[i];
 }
 
 // 16 int8 weights code*q from one packed word, k order
@@ -81,20 +91,26 @@ __device__ __forceinline__ v4i expand_word(uint32_t w, uint32_t table) {
   return r;
 }
 
-// one 128-wide group: 4 k-steps x (4 x 2) MFMA 32x32x32 tiles for this wave
-__device__ __forceinline__ void gemm_group(const GemmStage &st, const int8_t *sbuf, int l32, int h,
-                                           v16i (&acc)[4][2]) {
-  const uint32_t tab0 = perm_table(st.q[0]), tab1 = perm_table(st.q[1]);
+// one pair of groups: 8 k-steps x (4 x 2) MFMA 32x32x32 tiles for this wave.
+// k-step ss of group gi uses word 4h + ss of the lane's row: words 4h, 4h+1 sit in
+// the lane-quarter 2h slot of the tile, 4h+2, 4h+3 in the 2h+1 slot.
+__device__ __forceinline__ void gemm_pair(const GemmStage &st, const int8_t *sbuf, int l32, int h,
+                                          v16i (&acc)[4][2]) {
   const int8_t *abase = sbuf + l32 * kAStride + 64 * h;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const v4i bf0 = expand_word(st.b[0][s], tab0);
-    const v4i bf1 = expand_word(st.b[1][s], tab1);
+  for (int gi = 0; gi < 2; ++gi) {
+    const uint32_t tab0 = perm_table(st.q[0][gi]), tab1 = perm_table(st.q[1][gi]);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const v4i af = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + 16 * s);
-      acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mt][0], 0, 0, 0);
-      acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mt][1], 0, 0, 0);
+    for (int ss = 0; ss < 4; ++ss) {
+      const int slot = ss >> 1, word = 2 * gi + (ss & 1);
+      const v4i bf0 = expand_word(st.b[0][slot][word], tab0);
+      const v4i bf1 = expand_word(st.b[1][slot][word], tab1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const v4i af = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + kGroup * gi + 16 * ss);
+        acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mt][1], 0, 0, 0);
+      }
     }
   }
 }
@@ -111,26 +127,30 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   const int64_t m0 = int64_t(blockIdx.y) * kBM;
   const int64_t n0 = int64_t(blockIdx.x) * kBN;
   const int G = int(K / kGroup);
+  const int GP = (G + 1) / 2;
 
-  // activation staging: chunk c = tid + 256 i -> row c/8, 16-byte column c%8
-  const int8_t *asrc[4];
-  int adst[4];
+  // activation staging: chunk c = tid + 256 i -> row c/16, 16-byte column c%16
+  const int8_t *arow[8];
+  int acol[8], adst[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const int c = tid + kThreads * i;
-    const int row = c >> 3, c16 = c & 7;
+    const int row = c >> 4, c16 = c & 15;
     const int64_t m = m0 + row < M ? m0 + row : M - 1;
-    asrc[i] = xq + m * K + 16 * c16;
+    arow[i] = xq + m * K;
+    acol[i] = 16 * c16;
     adst[i] = row * kAStride + 16 * c16;
   }
-  // weight columns of this lane: one per 32-wide N tile
-  const char *bsrc[2];
+  // weight columns of this lane: one per 32-wide N tile, read from the packed tiles
+  const uint32_t *bsrc[2];
   const int8_t *qsrc[2];
+  const int64_t NB = (N + 15) / 16;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int64_t n = n0 + 64 * wave + 32 * j + l32;
     const int64_t nn = n < N ? n : N - 1;
-    bsrc[j] = reinterpret_cast<const char *>(packed) + nn * (K / 4) + 16 * h;
+    const int64_t rbg = nn / 16 < NB ? nn / 16 : NB - 1;
+    bsrc[j] = packed + 256 * (rbg * GP) + 4 * (32 * h + (nn & 15));
     qsrc[j] = q + nn * G;
   }
 
@@ -142,30 +162,30 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
 
-  // ring of kDepth groups of global loads in flight; slot d holds group g with
-  // g % kDepth == d.  Prefetches past the last group re-read group G-1 (valid
+  // ring of kDepth pairs of global loads in flight; slot d holds pair p with
+  // p % kDepth == d.  Prefetches past the last pair re-read pair GP-1 (valid
   // memory, discarded) so that the steady-state loop has no branches.
   GemmStage ring[kDepth];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load_stage(ring[d], min(d, G - 1), asrc, bsrc, qsrc);
+  for (int d = 0; d < kDepth; ++d) load_stage(ring[d], min(d, GP - 1), K, G, GP, arow, acol, bsrc, qsrc);
   stage_to_lds(&sA[0][0], ring[0], adst);
   __syncthreads();
 
-  const int full = G / kDepth * kDepth;
-  for (int g0 = 0; g0 < full; g0 += kDepth) {
+  const int full = GP / kDepth * kDepth;
+  for (int p0 = 0; p0 < full; p0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      const int g = g0 + d;
-      gemm_group(ring[d], &sA[d & 1][0], l32, h, acc);
-      load_stage(ring[d], min(g + kDepth, G - 1), asrc, bsrc, qsrc);
+      const int p = p0 + d;
+      gemm_pair(ring[d], &sA[d & 1][0], l32, h, acc);
+      load_stage(ring[d], min(p + kDepth, GP - 1), K, G, GP, arow, acol, bsrc, qsrc);
       stage_to_lds(&sA[(d + 1) & 1][0], ring[(d + 1) % kDepth], adst);
       __syncthreads();
     }
   }
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d) {
-    if (full + d < G) {
-      gemm_group(ring[d], &sA[d & 1][0], l32, h, acc);
+    if (full + d < GP) {
+      gemm_pair(ring[d], &sA[d & 1][0], l32, h, acc);
       stage_to_lds(&sA[(d + 1) & 1][0], ring[(d + 1) % kDepth], adst);
       __syncthreads();
     }

@@ -4,10 +4,11 @@
 // in {-1,0,+1}, one fp16 scale per row and 128-group) and "4. 効いた高速化"
 // (q[n,g] = round(127 s[n,g] / smax[n]) so that code * q is exact in int8).
 //
-// One workgroup per row.  The packed word layout (include/tl.h) puts code
-// 4r + b in byte b, bit pair r, so packing 16 int8 codes is four masks and
-// shifts: word = sum_r ((c_r & 0x03030303) << 2r), where c_r is the 32-bit word
-// holding codes 4r..4r+3.  Fields are the codes' two's-complement low bits.
+// The packed word encoding (include/tl.h) puts code 4r + b in byte b, bit pair
+// r, so packing 16 int8 codes is four masks and shifts:
+// word = sum_r ((c_r & 0x03030303) << 2r), where c_r is the 32-bit word holding
+// codes 4r..4r+3.  Fields are the codes' two's-complement low bits.  Words go to
+// the wavefront-shaped 1 KB tiles of the layout.
 // The scale decomposition takes the row maximum of |s|, then
 // q = RNE(fl32(fl32(127 s) / smax)): the quotient is formed in binary64 and
 // rounded to binary32 once, which equals the correctly rounded binary32 division
@@ -30,32 +31,43 @@ __device__ __forceinline__ int bad_bytes(uint32_t w) {
   return n;
 }
 
-__global__ __launch_bounds__(kThreads) void pack_rows_kernel(
-    const int8_t *__restrict__ codes, const uint16_t *__restrict__ scales, int64_t K,
-    uint32_t *__restrict__ packed, int8_t *__restrict__ q, float *__restrict__ row_scale,
-    int32_t *__restrict__ invalid_count) {
+// One workgroup per 1024-byte tile (rb, p): thread t builds word t of the tile,
+// which holds the 16 codes k = 128*(2p + gi) + 16*(2*(l/16) + m) + j of row
+// 16*rb + l%16, with l = t/4, gi = (t/2)%2, m = t%2.  Codes past N or K are the
+// zero padding of the layout.  Writes are one contiguous kilobyte per tile.
+__global__ __launch_bounds__(kThreads) void pack_tiles_kernel(const int8_t *__restrict__ codes,
+                                                              int64_t N, int64_t K, int GP,
+                                                              uint32_t *__restrict__ packed,
+                                                              int32_t *__restrict__ invalid_count) {
+  const int64_t tile = blockIdx.x;
+  const int64_t rb = tile / GP;
+  const int p = int(tile - rb * GP);
+  const int t = threadIdx.x;
+  const int l = t >> 2, gi = (t >> 1) & 1, m = t & 1;
+  const int64_t n = rb * 16 + (l & 15);
+  const int64_t k0 = 128 * (2 * int64_t(p) + gi) + 16 * (2 * (l >> 4) + m);
+  uint32_t word = 0;
+  int bad = 0;
+  if (n < N && k0 < K) {
+    const uint4 c = *reinterpret_cast<const uint4 *>(codes + n * K + k0);
+    word = (c.x & 0x03030303u) | ((c.y & 0x03030303u) << 2) | ((c.z & 0x03030303u) << 4) |
+           ((c.w & 0x03030303u) << 6);
+    if (invalid_count) bad = bad_bytes(c.x) + bad_bytes(c.y) + bad_bytes(c.z) + bad_bytes(c.w);
+  }
+  packed[tile * 256 + t] = word;
+  if (bad) atomicAdd(invalid_count, bad);
+}
+
+// One workgroup per row: smax = max_g |s|, q = RNE(fl32(127 s) / smax), row_scale.
+__global__ __launch_bounds__(kThreads) void scale_rows_kernel(const uint16_t *__restrict__ scales,
+                                                              int G, int8_t *__restrict__ q,
+                                                              float *__restrict__ row_scale) {
   __shared__ float red[kThreads / 64];
   const int64_t n = blockIdx.x;
-  const int nw = int(K / 16);
-  const int G = int(K / kGroup);
-  const int8_t *crow = codes + n * K;
-  uint32_t *prow = packed + n * int64_t(nw);
-
-  int bad = 0;
-  for (int w = threadIdx.x; w < nw; w += kThreads) {
-    const uint4 c = *reinterpret_cast<const uint4 *>(crow + 16 * w);
-    const uint32_t word = (c.x & 0x03030303u) | ((c.y & 0x03030303u) << 2) |
-                          ((c.z & 0x03030303u) << 4) | ((c.w & 0x03030303u) << 6);
-    if (invalid_count) bad += bad_bytes(c.x) + bad_bytes(c.y) + bad_bytes(c.z) + bad_bytes(c.w);
-    prow[w] = word;
-  }
-  if (invalid_count && bad) atomicAdd(invalid_count, bad);
-
   const uint16_t *srow = scales + n * G;
-  float m = 0.0f;
-  for (int g = threadIdx.x; g < G; g += kThreads) m = fmaxf(m, half_bits_to_float(srow[g] & 0x7FFFu));
-  const float smax = block_max<kThreads>(m, red);
-
+  float mx = 0.0f;
+  for (int g = threadIdx.x; g < G; g += kThreads) mx = fmaxf(mx, half_bits_to_float(srow[g] & 0x7FFFu));
+  const float smax = block_max<kThreads>(mx, red);
   int8_t *qrow = q + n * G;
   for (int g = threadIdx.x; g < G; g += kThreads) {
     int8_t qv = 0;
@@ -71,14 +83,21 @@ __global__ __launch_bounds__(kThreads) void pack_rows_kernel(
 
 }  // namespace
 
+int64_t packed_words(int64_t N, int64_t K) { return ((N + 15) / 16) * ((K + 255) / 256) * 256; }
+
 hipError_t launch_pack(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                        uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
                        hipStream_t stream) {
-  if (N > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t NB = (N + 15) / 16, GP = (K + 255) / 256;
+  if (NB * GP > 0x7FFFFFFF || N > 0x7FFFFFFF) return hipErrorInvalidValue;
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  hipLaunchKernelGGL(pack_rows_kernel, dim3(unsigned(N)), dim3(kThreads), 0, stream, codes, scales,
-                     K, packed, q, row_scale, invalid_count);
-  set_last_kernel("pack_rows");
+  hipLaunchKernelGGL(pack_tiles_kernel, dim3(unsigned(NB * GP)), dim3(kThreads), 0, stream, codes, N,
+                     K, int(GP), packed, invalid_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scale_rows_kernel, dim3(unsigned(N)), dim3(kThreads), 0, stream, scales,
+                     int(K / kGroup), q, row_scale);
+  set_last_kernel("pack_tiles+scale_rows");
   return hipGetLastError();
 }
 

@@ -71,6 +71,11 @@ const char *tl_last_kernel_name(void) { return tl::g_last_kernel; }
 
 const char *tl_last_error_detail(void) { return tl::g_last_error; }
 
+size_t tl_packed_bytes(int64_t N, int64_t K) {
+  if (N < 0 || K <= 0 || K % tl::kGroup || N >= kMaxDim || K >= kMaxDim) return 0;
+  return size_t(tl::packed_words(N, K)) * 4;
+}
+
 int tl_pack_weights(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                     uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
                     void *stream) {
@@ -82,7 +87,7 @@ int tl_pack_weights(const int8_t *codes, const uint16_t *scales, int64_t N, int6
     return TL_ERR_ALIGN;
   const size_t G = size_t(K / tl::kGroup);
   Span in[] = {{codes, size_t(N) * K}, {scales, size_t(N) * G * 2}};
-  Span out[] = {{packed, size_t(N) * (K / 16) * 4}, {q, size_t(N) * G}, {row_scale, size_t(N) * 4},
+  Span out[] = {{packed, size_t(tl::packed_words(N, K)) * 4}, {q, size_t(N) * G}, {row_scale, size_t(N) * 4},
                 {invalid_count, invalid_count ? 4u : 0u}};
   if (any_alias(in, 2, out, 4)) return TL_ERR_ALIAS;
   return from_hip(tl::launch_pack(codes, scales, N, K, packed, q, row_scale, invalid_count,
@@ -141,7 +146,7 @@ int tl_gemv_prepared(const void *workspace, size_t workspace_bytes, int64_t b, i
     return TL_ERR_ALIGN;
   const size_t G = size_t(K / tl::kGroup);
   const size_t ysz = size_t(b) * N * (y_dtype == TL_F32 ? 4 : 2);
-  Span in[] = {{workspace, need}, {packed, size_t(N) * (K / 16) * 4}, {scales, size_t(N) * G * 2}};
+  Span in[] = {{workspace, need}, {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2}};
   Span out[] = {{y, ysz}};
   if (any_alias(in, 3, out, 1)) return TL_ERR_ALIAS;
   return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype,
@@ -162,7 +167,7 @@ int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint
     return TL_ERR_ALIGN;
   const size_t G = size_t(K / tl::kGroup);
   const size_t ysz = size_t(b) * N * (y_dtype == TL_F32 ? 4 : 2);
-  Span in[] = {{xr, size_t(b) * K * 4}, {packed, size_t(N) * (K / 16) * 4}, {scales, size_t(N) * G * 2}};
+  Span in[] = {{xr, size_t(b) * K * 4}, {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2}};
   Span out[] = {{y, ysz}, {workspace, need}};
   if (any_alias(in, 3, out, 2)) return TL_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -205,7 +210,7 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
     return TL_ERR_ALIGN;
   const size_t G = size_t(K / tl::kGroup);
   const size_t ysz = size_t(M) * N * (y_dtype == TL_F32 ? 4 : 2);
-  Span in[] = {{xq, size_t(M) * K}, {tok_scale, size_t(M) * 4}, {packed, size_t(N) * (K / 16) * 4},
+  Span in[] = {{xq, size_t(M) * K}, {tok_scale, size_t(M) * 4}, {packed, size_t(tl::packed_words(N, K)) * 4},
                {q, size_t(N) * G}, {row_scale, size_t(N) * 4}};
   Span out[] = {{y, ysz}, {acc_out, acc_out ? size_t(M) * N * 4 : 0u}, {workspace, need}};
   if (any_alias(in, 5, out, 3)) return TL_ERR_ALIAS;

@@ -15,6 +15,7 @@ constexpr int kHBlock = 1024; // Hadamard block width
 // name of the last kernel launched by this host thread
 void set_last_kernel(const char *name);
 
+int64_t packed_words(int64_t N, int64_t K);
 hipError_t launch_pack(const int8_t *codes, const uint16_t *scales, int64_t N, int64_t K,
                        uint32_t *packed, int8_t *q, float *row_scale, int32_t *invalid_count,
                        hipStream_t stream);

@@ -36,7 +36,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tl.abi_version() == 1
+    assert tl.abi_version() == 2
+    assert tl.packed_words(16, 256) == 256 and tl.packed_words(17, 384) == 1024
+    assert tl.packed_words(40, 1024) == 3072 and tl.lib().tl_packed_bytes(4, 100) == 0
     for s in range(0, 9):
         assert tl.status_string(s)
     assert tl.status_string(0) == "ok"

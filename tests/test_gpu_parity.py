@@ -53,7 +53,7 @@ def test_pack_bit_exact(tl, name):
     d = dev()
     c, li, K, N = SHAPES[name]
     L = Layer(0, c, li, K, N, d)
-    packed = poison_(torch.empty((N, K // 16), dtype=torch.int32, device=d))
+    packed = poison_(torch.empty((tl.packed_words(N, K),), dtype=torch.int32, device=d))
     q = poison_(torch.empty((N, K // 128), dtype=torch.int8, device=d))
     rs = poison_(torch.empty((N,), dtype=torch.float32, device=d))
     bad = torch.zeros((1,), dtype=torch.int32, device=d)
@@ -65,7 +65,22 @@ def test_pack_bit_exact(tl, name):
     np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
     np.testing.assert_array_equal(rs.cpu().numpy().view(np.uint32), rs_ref.view(np.uint32))
     assert int(bad.item()) == 0
-    assert tl.last_kernel_name() == "pack_rows"
+    assert tl.last_kernel_name() == "pack_tiles+scale_rows"
+
+
+@pytest.mark.parametrize("N,K", [(7, 1024), (33, 384), (300, 128)])
+def test_pack_ragged_tiles(tl, N, K):
+    """Partial row blocks and an odd number of groups: padding words are zero."""
+    import torch
+    d = dev()
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    packed = poison_(torch.empty((tl.packed_words(N, K),), dtype=torch.int32, device=d))
+    announce(f"tl_pack_weights ragged N={N} K={K}")
+    tl.pack_weights(to_dev(codes, d), to_dev(scales, d), packed=packed)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), oracle.pack_codes(codes))
 
 
 def test_pack_edge_rows_and_bad_codes(tl):
@@ -195,7 +210,8 @@ def test_gemv_parity(tl, name, b):
     _gemv_case(tl, L, b, (c, li))
 
 
-@pytest.mark.parametrize("K,N,b", [(128, 300, 3), (256, 17, 16), (1024, 1000, 5), (3072, 64, 2)])
+@pytest.mark.parametrize("K,N,b", [(128, 300, 3), (256, 17, 16), (1024, 1000, 5), (3072, 64, 2),
+                                   (384, 33, 8), (17408, 48, 1), (5120, 100, 12)])
 def test_gemv_ragged(tl, K, N, b):
     """N not a multiple of the row tile, K smaller than the wave count, odd b."""
     import torch
@@ -276,7 +292,8 @@ def test_prefill_path_parity(tl, name, M):
     _gemm_check(tl, L.codes, L.scales, L.packed, L.q, L.rs, xq_ref, sx_ref, name)
 
 
-@pytest.mark.parametrize("M,K,N", [(77, 256, 300), (1, 128, 33), (130, 1024, 257), (129, 2048, 512)])
+@pytest.mark.parametrize("M,K,N", [(77, 256, 300), (1, 128, 33), (130, 1024, 257), (129, 2048, 512),
+                                   (64, 384, 96), (200, 640, 40)])
 def test_gemm_ragged(tl, M, K, N):
     d = dev()
     rng = np.random.default_rng(M * 31 + K + N)

@@ -159,25 +159,56 @@ def _decode_word_independently(w: int):
     return out
 
 
-def check_pack(pack, unpack):
+def _golden_tiles():
+    cases = []
+    for line in open(os.path.join(GOLD, "pack_tiles.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            lhs, rhs = line.split("|")
+            N, K, n, k, code = (int(v) for v in lhs.split())
+            total, index, value = rhs.split()
+            cases.append((N, K, n, k, code, int(total), int(index), int(value, 16)))
+    return cases
+
+
+def check_words(encode, decode):
     for codes, word in _golden_pack():
-        got = pack(np.array([codes], dtype=np.int8))
+        got = encode(np.array([codes], dtype=np.int8))
         assert got.shape == (1, 1) and int(got[0, 0]) == word, (codes, hex(int(got[0, 0])), hex(word))
     # all 3**8 patterns on j = 0..7 with a fixed upper half, then decoded twice
     pats = np.array(np.meshgrid(*[[-1, 0, 1]] * 8, indexing="ij")).reshape(8, -1).T
     upper = np.array([1, -1, 0, 0, 1, 1, -1, 0])
     codes = np.concatenate([pats, np.broadcast_to(upper, pats.shape)], axis=1).astype(np.int8)
-    words = pack(codes.reshape(-1, 16))[:, 0]
+    words = encode(codes.reshape(-1, 16))[:, 0]
     for i in range(0, len(words), 97):
         assert _decode_word_independently(int(words[i])) == codes[i].tolist()
-    np.testing.assert_array_equal(unpack(words[:, None], 16), codes)
-    # rows and words in order
+    np.testing.assert_array_equal(decode(words[:, None]), codes)
+
+
+def check_pack(pack, unpack):
+    for N, K, n, k, code, total, index, value in _golden_tiles():
+        c = np.zeros((N, K), dtype=np.int8)
+        c[n, k] = code
+        got = pack(c)
+        assert got.shape == (total,), (N, K, got.shape, total)
+        nz = np.nonzero(got)[0]
+        assert nz.tolist() == [index] and int(got[index]) == value, (N, K, n, k, nz, hex(int(got[nz[0]])))
+    # round trip with ragged N and an odd number of groups; every word decodes by hand
     rng = np.random.default_rng(5)
-    c = rng.integers(-1, 2, (7, 1024)).astype(np.int8)
-    p = pack(c)
-    assert p.shape == (7, 64)
-    for n, w in ((0, 0), (6, 63), (3, 17)):
-        assert _decode_word_independently(int(p[n, w])) == c[n, 16 * w:16 * w + 16].tolist()
+    for N, K in ((7, 1024), (33, 384), (16, 256)):
+        c = rng.integers(-1, 2, (N, K)).astype(np.int8)
+        p = pack(c)
+        np.testing.assert_array_equal(unpack(p, N, K), c)
+        # spot-check words against the index formula with the independent decoder
+        GP = -(-K // 256)
+        for n, w in ((0, 0), (N - 1, K // 16 - 1), (N // 2, 5)):
+            g, wi = w // 8, w % 8
+            idx = 256 * ((n // 16) * GP + g // 2) + 4 * (16 * (wi // 2) + n % 16) + 2 * (g % 2) + wi % 2
+            assert _decode_word_independently(int(p[idx])) == c[n, 16 * w:16 * w + 16].tolist()
+
+
+def test_word_pins():
+    check_words(oracle.encode_words, oracle.decode_words)
 
 
 def test_pack_pins():
@@ -406,6 +437,15 @@ def _pack_natural(codes):                         # natural bit order 2j
     return w.astype(np.uint32)
 
 
+def _pack_rowmajor(codes):                        # right words, row-major instead of tiles
+    codes = np.asarray(codes)
+    N, K = codes.shape
+    NB, GP = -(-N // 16), -(-K // 256)
+    padded = np.zeros((NB * 16, GP * 256), dtype=np.int8)
+    padded[:N, :K] = codes
+    return oracle.encode_words(padded).reshape(-1)
+
+
 def _decomp_half_up(scales):                      # round half away from zero
     s = np.asarray(scales, dtype=np.float16).astype(np.float32)
     smax = np.max(np.abs(s), axis=1)
@@ -436,7 +476,8 @@ def _gemm_transposed_q(xq, codes, q):             # q indexed by k % G instead o
     (lambda: check_hadamard(_had_or), "hadamard"),
     (lambda: check_rotation(_rot_no_norm), "rotation-norm"),
     (lambda: check_rotation(_rot_signs_after), "rotation-signs"),
-    (lambda: check_pack(_pack_natural, oracle.unpack_codes), "pack-order"),
+    (lambda: check_words(_pack_natural, oracle.decode_words), "word-bit-order"),
+    (lambda: check_pack(_pack_rowmajor, lambda p, N, K: oracle.decode_words(p.reshape(N, K // 16))), "pack-tile-order"),
     (lambda: check_scales(_decomp_half_up), "scale-ties"),
     (lambda: check_quant(_quant_mul_recip), "quant-formula"),
     (lambda: check_gemv(_gemv_wrong_group), "gemv-group"),
