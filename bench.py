@@ -39,6 +39,13 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 MALL_BYTES = 256 * 2 ** 20
 ROTATE_BYTES = 2 ** 30
 
+CALIB_BYTES = 64 * 2 ** 20    # the PMC calibration kernel reads and writes this many bytes
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "gemv": ("quantized_gemv_gemm_amd/csrc/k_gemv.hip", "quantized_gemv_gemm_amd/csrc/tl_device.h"),
+    "gemm": ("quantized_gemv_gemm_amd/csrc/k_gemm.hip", "quantized_gemv_gemm_amd/csrc/tl_device.h"),
+}
+
 DECODE_BS = (1, 4, 8, 16)
 PREFILL_M = 512
 DEC_LAYERS = 8     # qkv-shaped layers per decode pass (distinct weight copies)
@@ -58,11 +65,98 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calib-copy", action="store_true",
+                   help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
+    p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="write the HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                        "counter CSVs of this bench (--steps S --warmup W) and of --calib-copy, then exit")
     return p.parse_args()
+
+
+def source_hash(kind):
+    """sha256 of the sources a kernel family is built from (counters go stale when it changes)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _pmc_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+
+def _short_name(name):
+    """`gemv_lds_kernel<1, 1, 5>` out of a demangled kernel signature."""
+    import re
+    m = re.search(r"(\w+_kernel(?:<[^()]*>)?)\(", name)
+    return m.group(1) if m else name[:80]
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """HBM bytes per launch of the GEMV and GEMM kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE runs.
+
+    The counters read KiB per dispatch.  Each is scaled by the factor that makes
+    it read exactly CALIB_BYTES for the calibration kernel (an elementwise
+    negation of CALIB_BYTES of float32: CALIB_BYTES read, CALIB_BYTES written).
+    Launches are attributed by their order inside a step: 8 GEMV launches for
+    each b in DECODE_BS, then PRE_LAYERS GEMM launches for gate_up and for down.
+    """
+    def calib(path):
+        vals = [v for name, v in _pmc_rows(path) if "neg" in name]
+        if not vals:
+            raise SystemExit(f"no calibration dispatch in {path}")
+        return (CALIB_BYTES / 1024.0) / float(np.median(vals))
+
+    f_fac, w_fac = calib(copy_fetch_csv), calib(copy_write_csv)
+    out = {"copy_factor": {"fetch": round(f_fac, 4), "write": round(w_fac, 4)},
+           "sources": {k: source_hash(k) for k in KERNEL_SOURCES}, "gemv": {}, "gemm": {}}
+    for counter, path, fac in (("fetch", fetch_csv, f_fac), ("write", write_csv, w_fac)):
+        rows = _pmc_rows(path)
+        gemv = [(n, v) for n, v in rows if "gemv_lds_kernel" in n or "gemv_reg_kernel" in n]
+        gemm = [(n, v) for n, v in rows if "gemm_i8_kernel" in n]
+        if not gemv or len(gemv) % (DEC_LAYERS * len(DECODE_BS)) or not gemm or len(gemm) % (2 * PRE_LAYERS):
+            raise SystemExit(f"unexpected launch counts in {path}: {len(gemv)} GEMV, {len(gemm)} GEMM")
+        for i, (name, v) in enumerate(gemv):
+            b = str(DECODE_BS[(i // DEC_LAYERS) % len(DECODE_BS)])
+            e = out["gemv"].setdefault(b, {"kernel": _short_name(name), "fetch": [], "write": []})
+            e[counter].append(v * 1024.0 * fac)
+        for i, (name, v) in enumerate(gemm):
+            key = ("gate_up", "down")[(i // PRE_LAYERS) % 2]
+            e = out["gemm"].setdefault(key, {"kernel": _short_name(name), "fetch": [], "write": []})
+            e[counter].append(v * 1024.0 * fac)
+    for fam in ("gemv", "gemm"):
+        for e in out[fam].values():
+            e["launches"] = len(e["fetch"])
+            e["fetch_bytes"] = round(float(np.mean(e.pop("fetch"))))
+            e["write_bytes"] = round(float(np.mean(e.pop("write"))))
+            e["traffic_bytes"] = e["fetch_bytes"] + e["write_bytes"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def load_traffic():
+    """Per-launch HBM traffic measured for the current kernel sources, or {} if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return {}
+    return {fam: t[fam] for fam in KERNEL_SOURCES if t.get("sources", {}).get(fam) == source_hash(fam)}
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the "
               "single-GPU kernels; multi-GPU sharding is design-only.", file=sys.stderr)
@@ -76,6 +170,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tl.lib()
+
+    if args.calib_copy:
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(20):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_kernel": "neg float32", "bytes_read": CALIB_BYTES, "bytes_written": CALIB_BYTES,
+                          "launches": 20}))
+        return
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -204,6 +308,17 @@ def main():
         t_tot += t
     pre_tops = ops_tot / t_tot / 1e12
 
+    traffic = load_traffic()
+    gemv_traffic = gemm_traffic = None
+    if "gemv" in traffic and all(str(b) in traffic["gemv"] for b in DECODE_BS):
+        for b in DECODE_BS:
+            by_b[str(b)]["traffic_bytes"] = traffic["gemv"][str(b)]["traffic_bytes"]
+        gemv_traffic = round(float(np.mean([traffic["gemv"][str(b)]["traffic_bytes"] for b in DECODE_BS])))
+    if "gemm" in traffic and all(k in traffic["gemm"] for k in pre_out):
+        for k in pre_out:
+            pre_out[k]["traffic_bytes"] = traffic["gemm"][k]["traffic_bytes"]
+        gemm_traffic = round(float(np.mean([traffic["gemm"][k]["traffic_bytes"] for k in pre_out])))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle decode qkv b=16")
@@ -231,10 +346,11 @@ def main():
         "prefill_tops": round(pre_tops, 1),
         "prefill_gemm": pre_out,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": gemv_traffic,
+                     "algorithmic_bytes_per_launch": round(float(np.mean([gemv_bytes(b, Kq, Nq) for b in DECODE_BS]))),
                      "kernel": "GEMV weight stream (" + ", ".join(sorted({v["kernel"] for v in by_b.values()})) + ")"},
         "roofline_prefill": {"bound": "mfma", "achieved": round(pre_tops, 1), "peak": INT8_PEAK_TOPS,
-                             "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4)},
+                             "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
