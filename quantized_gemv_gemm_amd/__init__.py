@@ -247,6 +247,23 @@ def quant_act_int8(xr, xq=None, tok_scale=None):
     return xq, tok_scale
 
 
+_GEMM_WS = {}
+
+
+def _gemm_workspace(device, nbytes):
+    """A zero-filled GEMM workspace per (device, stream), grown on demand.
+
+    The kernels return the workspace's counters to zero at the end of every
+    call, so one buffer serves every call issued on that stream."""
+    import torch
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _GEMM_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros((nbytes,), dtype=torch.uint8, device=device)
+        _GEMM_WS[key] = ws
+    return ws
+
+
 def gemm_workspace_size(M: int, K: int, N: int) -> int:
     return int(lib().tl_gemm_workspace_size(M, K, N))
 
@@ -279,7 +296,7 @@ def gemm_int8_rescale(xq, tok_scale, packed, q, row_scale, out_dtype=None, out=N
             raise ValueError("acc_out must be [M, N]")
     need = gemm_workspace_size(M, K, N)
     if workspace is None and need:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=xq.device)
+        workspace = _gemm_workspace(xq.device, need)
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check("tl_gemm_int8_rescale", lib().tl_gemm_int8_rescale(
         _ptr(xq), _ptr(tok_scale), M, K, N, _ptr(packed), _ptr(q), _ptr(row_scale), _ptr(out), code,

@@ -10,17 +10,33 @@
 //
 // Tiling (CDNA4, v_mfma_i32_32x32x32_i8): a 256-thread workgroup computes a
 // 128 x 256 tile of y; each of its 4 waves owns 128 x 64 (4 x 2 MFMA tiles,
-// 128 int32 accumulators per lane).  The K loop steps one pair of 128-wide scale
-// groups at a time (8 MFMA k-steps), with two pairs of loads in flight.  The
-// activation tile (128 rows x 256 bytes) is staged in LDS, double buffered, and
-// shared by the 4 waves.  Each wave loads its own weight columns straight from
-// the packed tiles: two 16-byte loads per column per pair give the 8 words that
-// feed the pair's 8 k-steps.  The
-// expansion code -> code*q is one v_perm_b32 per 4 weights: the selector bytes
-// are the 2-bit fields ((w >> 2r) & 0x03030303) and the table holds
-// {0, q, -, -q}.  The packed layout puts codes 4r..4r+3 in bytes 0..3 of that
-// selector, in k order, so the weight fragment lines up with 16 consecutive
-// activation bytes read from LDS.
+// 128 int32 accumulators per lane), so every expanded weight fragment feeds four
+// MFMAs.  The K loop steps one pair of 128-wide scale groups (8 MFMA k-steps).
+//
+// Pipeline, per pair p:
+//  * the activation tile of pair p sits in one of three LDS buffers; the one of
+//    pair p+1 is already complete, the one of pair p+2 is written half way
+//    through pair p from registers loaded one pair earlier;
+//  * packed weight words arrive in a three-deep register ring (pairs p, p+1,
+//    p+2 in flight) and are loaded straight from the 1 KB packed tiles: two
+//    16-byte loads per column per pair;
+//  * inside a pair, the LDS reads and the weight expansion of k-step s+1 are
+//    issued between the MFMAs of k-step s, so neither LDS latency nor the
+//    expansion sits on the MFMA chain; one barrier per pair.
+// The expansion code -> code*q is one v_perm_b32 per 4 weights: the selector
+// bytes are the 2-bit fields ((w >> 2r) & 0x03030303) and the table holds
+// {0, q, -, -q}.
+//
+// Work distribution: the tiles are dealt out in whole rounds of kSlots
+// workgroups (one per compute unit), each round XCD-aware so that the four
+// M-blocks of one weight strip run on one XCD and share its L2.  The tiles left
+// over for a last, partial round are split along K into S pieces; every piece
+// stores its int32 partial tile to the workspace and bumps the tile's counter,
+// and the piece that arrives last adds the others and runs the epilogue
+// (integer sums: exact and order independent).  No workgroup ever waits for
+// another.
+#include <algorithm>
+
 #include "tl_device.h"
 
 namespace tl {
@@ -28,57 +44,41 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128;
 constexpr int kBN = 256;
 constexpr int kThreads = 256;
 constexpr int kPairK = 2 * kGroup;        // k per pipeline stage: one pair of groups
 constexpr int kAStride = kPairK + 16;     // LDS row pitch in bytes (padding spreads banks)
-constexpr int kDepth = 2;                 // pairs of global loads in flight per thread
+constexpr int kABuf = kBM * kAStride;     // one activation stage in LDS
+constexpr int kSlots = 256;               // workgroups per round: the compute units of gfx950
+constexpr int kXcds = 8;                  // workgroup i runs on XCD i % 8
+constexpr int kMaxSplit = 6;
+constexpr int kTileInts = kBM * kBN;
 
 static_assert(kBM * kPairK == kThreads * 8 * 16, "A stage = 8 x 16 bytes per thread");
 static_assert(kBN == 4 * 64, "4 waves x 64 columns");
+static_assert(kTileInts == kThreads * 128, "128 accumulators per thread");
 
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+struct BStage {
+  v4u w[2][2];  // [N tile][lane quarter 2h, 2h+1]: tile words for both groups of the pair
+  int q[2][2];  // [N tile][group of the pair], as loaded
+  uint32_t keep[2];  // per group of the pair: all ones, or 0 for a padding pair / missing group
+};
 
-struct GemmStage {
-  v4u a[8];     // this thread's eight 16-byte pieces of the 128 x 256 activation tile
-  v4u b[2][2];  // [N tile][lane quarter 2h, 2h+1]: tile words for both groups of the pair
-  int q[2][2];  // [N tile][group of the pair]
+struct Schedule {
+  int mb;         // M-blocks
+  int tiles;      // MB * N-strips
+  int full;       // tiles computed whole, in rounds of kSlots (the rest are split)
+  int split;      // pieces per left-over tile (1: nothing is split)
+  int64_t left() const { return split > 1 ? tiles - full : 0; }
+  int64_t grid() const { return full + left() * split; }
 };
 
 __device__ __forceinline__ uint32_t perm_table(int qv) {
   // bytes: [0] = 0, [1] = q, [2] = unused, [3] = -q
   return ((uint32_t)(uint8_t)(int8_t)(-qv) << 24) | ((uint32_t)(uint8_t)(int8_t)qv << 8);
-}
-
-// Loads are unconditional: rows past M and columns past N read a clamped, valid
-// address and their results are never stored.  With no divergent branches the
-// compiler can count outstanding loads exactly and keep kDepth pairs in flight.
-__device__ __forceinline__ void load_stage(GemmStage &st, int p, int64_t K, int G, int GP,
-                                           const int8_t *const (&arow)[8], const int (&acol)[8],
-                                           const uint32_t *const (&bsrc)[2],
-                                           const int8_t *const (&qsrc)[2]) {
-  const int64_t koff = int64_t(p) * kPairK;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // the padded half of a last odd pair re-reads the row's last group (zero weights)
-    const int64_t o = koff + acol[i] < K ? koff + acol[i] : koff + acol[i] - kGroup;
-    st.a[i] = *reinterpret_cast<const v4u *>(arow[i] + o);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t *t = bsrc[j] + 256 * int64_t(p);
-    st.b[j][0] = *reinterpret_cast<const v4u *>(t);
-    st.b[j][1] = *reinterpret_cast<const v4u *>(t + 64);
-    st.q[j][0] = (int)qsrc[j][2 * p];
-    st.q[j][1] = 2 * p + 1 < G ? (int)qsrc[j][2 * p + 1] : 0;
-  }
-}
-
-__device__ __forceinline__ void stage_to_lds(int8_t *buf, const GemmStage &st, const int (&adst)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u *>(buf + adst[i]) = st.a[i];
 }
 
 // 16 int8 weights code*q from one packed word, k order
@@ -91,67 +91,242 @@ __device__ __forceinline__ v4i expand_word(uint32_t w, uint32_t table) {
   return r;
 }
 
-// one pair of groups: 8 k-steps x (4 x 2) MFMA 32x32x32 tiles for this wave.
-// k-step ss of group gi uses word 4h + ss of the lane's row: words 4h, 4h+1 sit in
-// the lane-quarter 2h slot of the tile, 4h+2, 4h+3 in the 2h+1 slot.
-__device__ __forceinline__ void gemm_pair(const GemmStage &st, const int8_t *sbuf, int l32, int h,
+// Per-thread addressing, fixed for the whole tile.  All global reads go through
+// buffer resources that cover exactly the tile's rows of xq, its packed row
+// blocks and its q rows: a read past M, past N or past the last group returns
+// zeros, which only ever meets zero weights or results that are not stored.
+struct Frame {
+  __amdgpu_buffer_rsrc_t ra, rb, rq;
+  int aoff;       // byte offset of this thread's first staged activation piece
+  int astep;      // 16 rows of activations, in bytes
+  int adst;       // LDS offset of the first piece; piece i is 16 rows further
+  int boff[2];    // this lane's 16 bytes of the first tile of its weight column, per N tile
+  int qoff[2];    // q row of that column
+  int G;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+
+__device__ __forceinline__ void load_a(v4u (&a)[8], const Frame &f, int p) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    a[i] = __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.aoff, p * kPairK + i * f.astep, 0);
+}
+
+__device__ __forceinline__ void load_b(BStage &b, const Frame &f, int p, bool live) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    b.w[j][0] = __builtin_amdgcn_raw_buffer_load_b128(f.rb, f.boff[j], p * 1024, 0);
+    b.w[j][1] = __builtin_amdgcn_raw_buffer_load_b128(f.rb, f.boff[j] + 256, p * 1024, 0);
+    b.q[j][0] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(f.rq, f.qoff[j], 2 * p, 0);
+    b.q[j][1] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(f.rq, f.qoff[j] + 1, 2 * p, 0);
+  }
+  // a padding pair (live == false) and the missing half of a last odd pair expand
+  // to zero weights; the mask is applied at expansion so that no instruction here
+  // waits for the loads
+  b.keep[0] = live ? ~0u : 0u;
+  b.keep[1] = live && 2 * p + 1 < f.G ? ~0u : 0u;
+}
+
+__device__ __forceinline__ void store_a(int8_t *buf, const v4u (&a)[8], const Frame &f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u *>(buf + f.adst + 16 * kAStride * i) = a[i];
+}
+
+// k-step s (0..7) of a pair: group gi = s / 4, sub-step ss = s % 4.  Word 4h + ss
+// of the lane's column in group gi: words 4h, 4h+1 sit in the lane-quarter 2h slot
+// of the tile, 4h+2, 4h+3 in the 2h+1 slot.
+__device__ __forceinline__ void fetch_a(v4i (&af)[4], const int8_t *abase, int s) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    af[mt] = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + kGroup * (s >> 2) + 16 * (s & 3));
+}
+
+__device__ __forceinline__ void fetch_b(v4i (&bf)[2], const BStage &b, int s) {
+  const int gi = s >> 2, ss = s & 3;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    bf[j] = expand_word(b.w[j][ss >> 1][2 * gi + (ss & 1)], perm_table(b.q[j][gi]) & b.keep[gi]);
+}
+
+__device__ __forceinline__ void mfma_step(const v4i (&af)[4], const v4i (&bf)[2], v16i (&acc)[4][2]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[0], acc[mt][0], 0, 0, 0);
+    acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[1], acc[mt][1], 0, 0, 0);
+  }
+}
+
+// One pair p.  Weight ring slot S = (p - p0) mod 4 is fixed at compile time; the
+// LDS buffer lb = (p - p0) mod 3 is a run-time offset.  On entry af[0] / bf[0]
+// hold k-step 0 of pair p, the LDS buffer of pair p+1 is complete, anext[S & 1]
+// holds (or is loading) the activation stage of pair p+2 and anext[~S & 1] that
+// of p+3, and the ring holds (or is loading) pairs p+1..p+3.  On exit the same
+// holds for p+1.  Pairs before k0 are padding
+// (zero weights), data indices are clamped into [k0, k1).
+template <int S>
+__device__ __forceinline__ void pair_body(int p, int k0, int plast, int &lb, const Frame &f,
+                                          int8_t *lds, const int8_t *aread, BStage (&ring)[4],
+                                          v4u (&anext)[2][8], v4i (&af)[2][4], v4i (&bf)[2][2],
                                           v16i (&acc)[4][2]) {
-  const int8_t *abase = sbuf + l32 * kAStride + 64 * h;
+  constexpr int S1 = (S + 1) % 4;
+  const int lb1 = lb == 2 ? 0 : lb + 1, lb2 = lb1 == 2 ? 0 : lb1 + 1;
+  const int8_t *cur = aread + lb * kABuf;
+  const int8_t *nxt = aread + lb1 * kABuf;
+  // Scheduling fences keep the issue order: LDS reads for k-step s+1, then the
+  // MFMAs of k-step s interleaved with the expansion for s+1, then stage traffic.
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const uint32_t tab0 = perm_table(st.q[0][gi]), tab1 = perm_table(st.q[1][gi]);
+  for (int s = 0; s < 8; ++s) {
+    if (s < 7)
+      fetch_a(af[(s + 1) & 1], cur, s + 1);
+    else
+      fetch_a(af[0], nxt, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(af[s & 1], bf[s & 1], acc);
+    if (s < 7)
+      fetch_b(bf[(s + 1) & 1], ring[S], s + 1);
+    else
+      fetch_b(bf[0], ring[S1], 0);
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      const int slot = ss >> 1, word = 2 * gi + (ss & 1);
-      const v4i bf0 = expand_word(st.b[0][slot][word], tab0);
-      const v4i bf1 = expand_word(st.b[1][slot][word], tab1);
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s == 3) {
+      store_a(lds + lb2 * kABuf, anext[S & 1], f);
+      load_a(anext[S & 1], f, min(max(p + 4, k0), plast));
+    }
+    if (s == 7) load_b(ring[S], f, min(max(p + 4, k0), plast), p + 4 >= k0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  lb = lb1;
+  __syncthreads();
+}
+
+// Tiles are dealt out in whole rounds of kSlots; the tiles left over for a last,
+// partial round are split into S pieces along K when that shortens the round.
+// Cost of a piece in pair-steps: its pairs rounded up to the ring turn of 4, plus
+// about one pair-step per partial tile the last piece has to add (128 KB each).
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// y = fl32(fl32(acc) * row_scale[n]) * tok_scale[m].  The lane holds column l32 of
+// each 32x32 tile, rows 8*(r/4) + 4*h + r%4: four consecutive rows per r/4, whose
+// token scales come from LDS in one 16-byte read.  A tile that lies inside
+// [M, N] takes the variant without per-element bounds tests.
+template <bool kCheck, bool kF32>
+__device__ __forceinline__ void epilogue(const v16i (&acc)[4][2], const float *s_tok,
+                                         const float (&rsv)[2], int64_t m0, int64_t n0, int64_t M,
+                                         int64_t N, int wave, int l32, int h, void *y,
+                                         int32_t *acc_out) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const v4i af = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + kGroup * gi + 16 * ss);
-        acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, acc[mt][1], 0, 0, 0);
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + 64 * wave + 32 * j + l32;
+    if (kCheck && n >= N) continue;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int row = 32 * mt + 8 * rq + 4 * h;
+        const v4f ts = *reinterpret_cast<const v4f *>(s_tok + row);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m0 + row + i;
+          if (kCheck && m >= M) continue;
+          const int a = acc[mt][j][4 * rq + i];
+          const float v = ((float)a * rsv[j]) * ts[i];
+          const int64_t o = m * N + n;
+          if (acc_out) acc_out[o] = a;
+          if (kF32)
+            reinterpret_cast<float *>(y)[o] = v;
+          else
+            reinterpret_cast<uint16_t *>(y)[o] = float_to_bf16_bits(v);
+        }
       }
+  }
+}
+
+inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
+  Schedule sc;
+  sc.mb = int((M + kBM - 1) / kBM);
+  sc.tiles = sc.mb * int((N + kBN - 1) / kBN);
+  const int left = sc.tiles % kSlots;
+  int best = 1;
+  if (left) {
+    int64_t best_cost = (GP + 3) / 4 * 4;
+    for (int S = 2; S <= kMaxSplit && S * left <= kSlots && S <= GP; ++S) {
+      const int64_t piece = (GP + S - 1) / S;
+      const int64_t cost = (piece + 3) / 4 * 4 + (S - 1);
+      if (cost < best_cost) best_cost = cost, best = S;
     }
   }
+  sc.split = best;
+  sc.full = best > 1 ? sc.tiles - left : sc.tiles;
+  return sc;
 }
 
 __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int64_t M, int64_t K,
     int64_t N, const uint32_t *__restrict__ packed, const int8_t *__restrict__ q,
     const float *__restrict__ row_scale, void *__restrict__ y, int y_dtype,
-    int32_t *__restrict__ acc_out) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[2][kBM * kAStride];
+    int32_t *__restrict__ acc_out, int32_t *__restrict__ part, int32_t *__restrict__ counters,
+    Schedule sc) {
+  __shared__ __attribute__((aligned(16))) int8_t sA[3 * kABuf];
+  __shared__ __attribute__((aligned(16))) float s_tok[kBM];
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int64_t m0 = int64_t(blockIdx.y) * kBM;
-  const int64_t n0 = int64_t(blockIdx.x) * kBN;
   const int G = int(K / kGroup);
   const int GP = (G + 1) / 2;
 
-  // activation staging: chunk c = tid + 256 i -> row c/16, 16-byte column c%16
-  const int8_t *arow[8];
-  int acol[8], adst[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c >> 4, c16 = c & 15;
-    const int64_t m = m0 + row < M ? m0 + row : M - 1;
-    arow[i] = xq + m * K;
-    acol[i] = 16 * c16;
-    adst[i] = row * kAStride + 16 * c16;
+  // which tile and which K range this workgroup computes
+  const int g = blockIdx.x;
+  int tile, piece = 0, k0 = 0, k1 = GP;
+  if (g < sc.full) {
+    const int round = g / kSlots, u = g % kSlots;
+    tile = (kSlots % kXcds == 0 && sc.full - round * kSlots >= kSlots)
+               ? round * kSlots + (kSlots / kXcds) * (u % kXcds) + u / kXcds
+               : g;
+  } else {
+    const int e = g - sc.full;
+    tile = sc.full + e / sc.split;
+    piece = e % sc.split;
+    k0 = int(int64_t(GP) * piece / sc.split);
+    k1 = int(int64_t(GP) * (piece + 1) / sc.split);
   }
+  const int64_t m0 = int64_t(tile % sc.mb) * kBM;
+  const int64_t n0 = int64_t(tile / sc.mb) * kBN;
+
+  Frame f;
+  f.G = G;
+  {
+    const int64_t rows = M - m0 < kBM ? M - m0 : kBM;
+    f.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(xq + m0 * K), (short)0,
+                                             int(rows * K), kRsrcWord3);
+    const int64_t NB = (N + 15) / 16, rb0 = n0 / 16;
+    const int64_t blocks = NB - rb0 < kBN / 16 ? NB - rb0 : kBN / 16;
+    f.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(packed + 256 * rb0 * GP), (short)0,
+                                             int(blocks * GP * 1024), kRsrcWord3);
+    const int64_t cols = N - n0 < kBN ? N - n0 : kBN;
+    f.rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(q + n0 * G), (short)0, int(cols * G),
+                                             kRsrcWord3);
+  }
+  // activation staging: chunk c = tid + 256 i -> row c/16 = tid/16 + 16 i, 16-byte column tid%16
+  f.aoff = int((tid >> 4) * K) + 16 * (tid & 15);
+  f.astep = int(16 * K);
+  f.adst = (tid >> 4) * kAStride + 16 * (tid & 15);
+  // token scales of the tile's rows (LDS, read in the epilogue) and this lane's row scales
+  if (tid < kBM) s_tok[tid] = tok_scale[m0 + tid < M ? m0 + tid : M - 1];
+  float rsv[2];
   // weight columns of this lane: one per 32-wide N tile, read from the packed tiles
-  const uint32_t *bsrc[2];
-  const int8_t *qsrc[2];
-  const int64_t NB = (N + 15) / 16;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + 64 * wave + 32 * j + l32;
-    const int64_t nn = n < N ? n : N - 1;
-    const int64_t rbg = nn / 16 < NB ? nn / 16 : NB - 1;
-    bsrc[j] = packed + 256 * (rbg * GP) + 4 * (32 * h + (nn & 15));
-    qsrc[j] = q + nn * G;
+    const int c = 64 * wave + 32 * j + l32;         // column inside the tile
+    f.boff[j] = (c >> 4) * GP * 1024 + 16 * (32 * h + (c & 15));
+    f.qoff[j] = c * G;
+    const int64_t n = n0 + c;
+    rsv[j] = row_scale[n < N ? n : N - 1];
   }
 
   v16i acc[4][2];
@@ -162,72 +337,115 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
 
-  // ring of kDepth pairs of global loads in flight; slot d holds pair p with
-  // p % kDepth == d.  Prefetches past the last pair re-read pair GP-1 (valid
-  // memory, discarded) so that the steady-state loop has no branches.
-  GemmStage ring[kDepth];
+  // The pair count is padded up to a multiple of 4 with leading zero-weight
+  // pairs, so that the loop below only exits after a whole ring turn.
+  // prologue: LDS buffers 0 and 1 <- pairs p0, p0+1; registers <- pair p0+2;
+  // weight ring <- pairs p0 .. p0+3.  Indices are clamped into [k0, k1) (valid
+  // memory; a clamped copy is either padding or never used).
+  const int plast = k1 - 1;
+  const int p0 = k0 - ((4 - (k1 - k0) % 4) % 4);
+  BStage ring[4];
+  v4u anext[2][8];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load_stage(ring[d], min(d, GP - 1), K, G, GP, arow, acol, bsrc, qsrc);
-  stage_to_lds(&sA[0][0], ring[0], adst);
+  for (int i = 0; i < 4; ++i) load_b(ring[i], f, min(max(p0 + i, k0), plast), p0 + i >= k0);
+  load_a(anext[0], f, k0);
+  load_a(anext[1], f, min(max(p0 + 1, k0), plast));
+  store_a(sA, anext[0], f);
+  load_a(anext[0], f, min(max(p0 + 2, k0), plast));
+  store_a(sA + kABuf, anext[1], f);
+  load_a(anext[1], f, min(max(p0 + 3, k0), plast));
   __syncthreads();
 
-  const int full = GP / kDepth * kDepth;
-  for (int p0 = 0; p0 < full; p0 += kDepth) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int p = p0 + d;
-      gemm_pair(ring[d], &sA[d & 1][0], l32, h, acc);
-      load_stage(ring[d], min(p + kDepth, GP - 1), K, G, GP, arow, acol, bsrc, qsrc);
-      stage_to_lds(&sA[(d + 1) & 1][0], ring[(d + 1) % kDepth], adst);
-      __syncthreads();
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d) {
-    if (full + d < GP) {
-      gemm_pair(ring[d], &sA[d & 1][0], l32, h, acc);
-      stage_to_lds(&sA[(d + 1) & 1][0], ring[(d + 1) % kDepth], adst);
-      __syncthreads();
-    }
+  const int8_t *aread = sA + l32 * kAStride + 64 * h;
+  v4i af[2][4], bf[2][2];
+  fetch_a(af[0], aread, 0);
+  fetch_b(bf[0], ring[0], 0);
+
+  int lb = 0;
+  for (int p = p0; p < k1; p += 4) {
+    pair_body<0>(p, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+    pair_body<1>(p + 1, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+    pair_body<2>(p + 2, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+    pair_body<3>(p + 3, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
   }
 
-  // epilogue: lane holds column l32 of each 32x32 tile, rows 8*(r/4) + 4*h + r%4
+  if (g >= sc.full) {
+    // Split tile: publish this piece, and only the last piece to arrive goes on.
+    // Partials are written and read with device-scope atomic accesses (written
+    // through to, and read from, the point where all XCDs are coherent), so no
+    // whole-L2 fence is needed: the stores are waited for before the counter is
+    // bumped, and the reads are issued after the counter has answered.
+    const int slot = g - sc.full;                      // piece index among the left-over tiles
+    int32_t *mine = part + int64_t(slot) * kTileInts;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + 64 * wave + 32 * j + l32;
-    if (n >= N) continue;
-    const float rs = row_scale[n];
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m >= M) continue;
-        const int a = acc[mt][j][r];
-        const float v = ((float)a * rs) * tok_scale[m];
-        if (acc_out) acc_out[m * N + n] = a;
-        if (y_dtype == TL_F32)
-          reinterpret_cast<float *>(y)[m * N + n] = v;
-        else
-          reinterpret_cast<uint16_t *>(y)[m * N + n] = float_to_bf16_bits(v);
-      }
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(&mine[((mt * 2 + j) * 16 + r) * kThreads + tid], acc[mt][j][r],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every partial store has completed
+    __syncthreads();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(&counters[tile - sc.full], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old == sc.split - 1;
     }
+    __syncthreads();
+    if (!s_last) return;
+    const int first = slot - piece;
+    for (int o = 0; o < sc.split; ++o) {
+      if (o == piece) continue;
+      int32_t *other = part + int64_t(first + o) * kTileInts;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[mt][j][r] += __hip_atomic_load(&other[((mt * 2 + j) * 16 + r) * kThreads + tid],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0)  // leave the workspace as it was found
+      __hip_atomic_store(&counters[tile - sc.full], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  const bool whole = m0 + kBM <= M && n0 + kBN <= N;
+  if (y_dtype == TL_F32) {
+    if (whole) epilogue<false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
+    else epilogue<true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
+  } else {
+    if (whole) epilogue<false, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
+    else epilogue<true, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
   }
 }
 
+constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t /*M*/, int64_t /*K*/, int64_t /*N*/) { return 0; }
+size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const Schedule s = make_schedule(M, N, (K / kGroup + 1) / 2);
+  if (s.split <= 1) return 0;
+  return align256(size_t(s.left()) * 4) + size_t(s.left() * s.split) * kTileInts * 4;
+}
 
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
                        const uint32_t *packed, const int8_t *q, const float *row_scale, void *y,
-                       int y_dtype, int32_t *acc_out, void * /*workspace*/, hipStream_t stream) {
-  const int64_t gx = (N + kBN - 1) / kBN, gy = (M + kBM - 1) / kBM;
-  if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidValue;
+                       int y_dtype, int32_t *acc_out, void *workspace, hipStream_t stream) {
+  if ((M + kBM - 1) / kBM * ((N + kBN - 1) / kBN) > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const Schedule s = make_schedule(M, N, (K / kGroup + 1) / 2);
+  int32_t *counters = nullptr, *part = nullptr;
+  if (s.split > 1) {
+    counters = static_cast<int32_t *>(workspace);
+    part = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + align256(size_t(s.left()) * 4));
+  }
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(gx), unsigned(gy)), dim3(kThreads), 0, stream,
-                     xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype, acc_out);
-  set_last_kernel("gemm_i8_mfma32_128x256");
+  hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
+                     M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
+  set_last_kernel(s.split > 1 ? "gemm_i8_mfma32_128x256_splitk" : "gemm_i8_mfma32_128x256");
   return hipGetLastError();
 }
 

@@ -202,12 +202,12 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
   if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
   if (M == 0 || N == 0) return TL_OK;
   if (!xq || !tok_scale || !packed || !q || !row_scale || !y) return TL_ERR_NULLPTR;
-  const size_t need = tl::gemm_workspace_bytes(M, K, N);
-  if (need && (!workspace || workspace_bytes < need)) return TL_ERR_WORKSPACE;
   if (!aligned16(xq) || !aligned16(tok_scale) || !aligned16(packed) || !aligned16(q) ||
       !aligned16(row_scale) || !aligned16(y) || (acc_out && !aligned16(acc_out)) ||
-      (need && !aligned16(workspace)))
+      (workspace && !aligned16(workspace)))
     return TL_ERR_ALIGN;
+  const size_t need = tl::gemm_workspace_bytes(M, K, N);
+  if (need && (!workspace || workspace_bytes < need)) return TL_ERR_WORKSPACE;
   const size_t G = size_t(K / tl::kGroup);
   const size_t ysz = size_t(M) * N * (y_dtype == TL_F32 ? 4 : 2);
   Span in[] = {{xq, size_t(M) * K}, {tok_scale, size_t(M) * 4}, {packed, size_t(tl::packed_words(N, K)) * 4},
