@@ -36,6 +36,8 @@
 //    weights, two pairs in flight, and are shared by RB row blocks.
 // Rows past N and token slots past b read clamped, valid addresses (no divergent
 // branches around loads) and their results are never stored.
+#include <algorithm>
+
 #include "tl_device.h"
 
 namespace tl {
@@ -126,9 +128,15 @@ __device__ __forceinline__ v4i unpack_x64(uint32_t w) {
 // epilogue only touches the first ceil(b/4) accumulators.
 __device__ __forceinline__ int token_of_arow(int r) { return 4 * (r & 3) + (r >> 2); }
 
+// Paired-limb mode (LP, for b <= 8): A row r holds limb r%2 (0 = hi, 1 = lo) of
+// token 2*(r/4) + (r/2)%2, so a single MFMA chain yields both limb sums of a token
+// in one lane -- D rows 4q, 4q+1 are hi, lo of token 2q and 4q+2, 4q+3 those of
+// token 2q+1 -- which halves the MFMAs and activation reads of the two-limb form.
+__device__ __forceinline__ int lp_token(int r) { return 2 * (r >> 2) + ((r >> 1) & 1); }
+
 // one group for RB row blocks: two 64-k halves x two limbs, then f32 accumulation.
 // w0/w1 are the lane's packed words for the group's two 64-k halves.
-template <int RB, int NT>
+template <int RB, int NT, bool LP>
 __device__ __forceinline__ void group_mfma(const v4i (&ah)[2], const v4i (&al)[2],
                                            const uint32_t (&w0)[RB], const uint32_t (&w1)[RB],
                                            const float (&s)[RB], float (&acc)[RB][4]) {
@@ -137,6 +145,13 @@ __device__ __forceinline__ void group_mfma(const v4i (&ah)[2], const v4i (&al)[2
     const v4i z = {0, 0, 0, 0};
     const v4i b0 = unpack_x64(w0[rb]);
     const v4i b1 = unpack_x64(w1[rb]);
+    if (LP) {
+      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[0], b0, z, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[1], b1, d, 0, 0, 0);
+      acc[rb][0] = fmaf(s[rb], (float)(d[0] * 256 + d[1]), acc[rb][0]);
+      acc[rb][1] = fmaf(s[rb], (float)(d[2] * 256 + d[3]), acc[rb][1]);
+      continue;
+    }
     v4i dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[0], b0, z, 0, 0, 0);
     v4i dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[0], b0, z, 0, 0, 0);
     dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[1], b1, dh, 0, 0, 0);
@@ -147,7 +162,7 @@ __device__ __forceinline__ void group_mfma(const v4i (&ah)[2], const v4i (&al)[2
 }
 
 // both groups of a pair: tile words .x/.y feed group 2p, .z/.w group 2p+1
-template <int RB, int NT>
+template <int RB, int NT, bool LP>
 __device__ __forceinline__ void pair_mfma(const v4i (&ah)[2][2], const v4i (&al)[2][2],
                                           const uint4 (&w)[RB], const float (&s)[2][RB],
                                           float (&acc)[RB][4]) {
@@ -159,8 +174,8 @@ __device__ __forceinline__ void pair_mfma(const v4i (&ah)[2][2], const v4i (&al)
     b0[rb] = w[rb].z;
     b1[rb] = w[rb].w;
   }
-  group_mfma<RB, NT>(ah[0], al[0], a0, a1, s[0], acc);
-  group_mfma<RB, NT>(ah[1], al[1], b0, b1, s[1], acc);
+  group_mfma<RB, NT, LP>(ah[0], al[0], a0, a1, s[0], acc);
+  group_mfma<RB, NT, LP>(ah[1], al[1], b0, b1, s[1], acc);
 }
 
 // the lane's 16 bytes of tile (row block rbg, pair p): one coalesced kilobyte per wave
@@ -169,16 +184,80 @@ __device__ __forceinline__ uint4 load_tile(const uint32_t *__restrict__ packed, 
   return *reinterpret_cast<const uint4 *>(packed + 256 * (rbg * GP + p) + 4 * lane);
 }
 
-// group scales of the lane's row for groups 2p and 2p+1 (0 past the last group)
-__device__ __forceinline__ void load_pair_scales(const uint16_t *__restrict__ srow, int G, int p,
-                                                 float &s0, float &s1) {
-  const int g0 = 2 * p, g1 = 2 * p + 1;
-  s0 = half_bits_to_float(srow[g0]);
-  s1 = g1 < G ? half_bits_to_float(srow[g1]) : 0.0f;
+// The fp16 scales of the workgroup's 16*RB rows are one contiguous run of the
+// row-major [N, G] array: it is copied into LDS with 1 KB direct loads (chunk c
+// by wave c mod W) in the same memory round as the weights, instead of two scattered
+// 2-byte loads per lane and pair.  Pieces past the end of the array read a
+// clamped, valid address; those LDS bytes lie beyond the run and are never read.
+__device__ __forceinline__ void stage_scales(const uint16_t *__restrict__ scales, int64_t N, int G,
+                                             int64_t n0, int rows, char *ls, int wave, int W,
+                                             int lane) {
+  if (n0 + rows > N) {
+    // the last workgroup holds fewer rows: its run may end inside a 16-byte piece
+    const int64_t valid = (N - n0) * G;
+    for (int64_t e = 64 * wave + lane; e < valid; e += 64 * W)
+      reinterpret_cast<uint16_t *>(ls)[e] = scales[n0 * G + e];
+    return;
+  }
+  // a whole run ends on a 32-byte boundary: every piece it needs lies inside the array
+  const int64_t begin = n0 * G * 2, total = N * G * 2;
+  const int chunks = (rows * G * 2 + 1023) / 1024;
+  for (int c = wave; c < chunks; c += W) {
+    const int64_t off = begin + int64_t(c) * 1024 + 16 * lane;
+    const int64_t src = off + 16 <= total ? off : 0;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(scales) + src,
+                                     (__attribute__((address_space(3))) void *)(ls + c * 1024), 16, 0,
+                                     0);
+  }
+}
+
+// group scales of local row r for groups 2p and 2p+1 (0 past the last group), from LDS
+__device__ __forceinline__ void pair_scales_lds(const char *ls, int r, int G, int p, float &s0,
+                                                float &s1) {
+  const uint16_t *row = reinterpret_cast<const uint16_t *>(ls) + r * G;
+  s0 = half_bits_to_float(row[2 * p]);
+  s1 = 2 * p + 1 < G ? half_bits_to_float(row[2 * p + 1]) : 0.0f;
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n), lgkmcnt(0), expcnt left free
+template <int n>
+constexpr int waitcnt_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4);
+}
+
+// LDS reads the compiler does not track; lds_wait() waits for them and ties the
+// values to that wait, so nothing uses them earlier
+__device__ __forceinline__ v4i lds_read16(const int8_t *p) {
+  v4i r;
+  asm volatile("ds_read_b128 %0, %1"
+               : "=v"(r)
+               : "v"((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t *)p));
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_read_u16(const char *p) {
+  uint32_t r;
+  asm volatile("ds_read_u16 %0, %1"
+               : "=v"(r)
+               : "v"((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p));
+  return r;
+}
+template <int RB>
+__device__ __forceinline__ void lds_wait(v4i (&ah)[2][2], v4i (&al)[2][2], uint32_t (&sb)[2][RB],
+                                         bool lp) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(ah[0][0]), "+v"(ah[0][1]), "+v"(ah[1][0]), "+v"(ah[1][1]));
+  if (!lp) asm volatile("" : "+v"(al[0][0]), "+v"(al[0][1]), "+v"(al[1][0]), "+v"(al[1][1]));
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(sb[0][rb]), "+v"(sb[1][rb]));
+}
+
+__host__ __device__ constexpr int scale_lds_bytes(int rows, int G) {
+  return (rows * G * 2 + 1023) / 1024 * 1024;
 }
 
 // partial sums of the W waves -> LDS -> wave 0 scales by sigma/64 and stores
-template <int RB, int NT>
+template <int RB, int NT, bool LP>
 __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red, int W, int wave,
                                                  int lane, int b, int64_t n0, int64_t N,
                                                  const float *__restrict__ sigma, void *y,
@@ -201,7 +280,7 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red
   }
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const int t = 4 * i + qd;  // token held by D row 4*qd + i
+    const int t = LP ? 2 * qd + i : 4 * i + qd;  // token of accumulator i
     if (t >= b) continue;
     const float sc = sigma[t] * (1.0f / 64.0f);
 #pragma unroll
@@ -218,115 +297,180 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red
 }
 
 // --------------------------------------------------------------------------
-// gemv_lds: limbs staged in LDS, every weight load of a wave issued up front
+// gemv_stream: every load of the wave issued at once, pairs consumed as they land
 // --------------------------------------------------------------------------
-template <int RB, int NT, int PMAX>
-__global__ __launch_bounds__(1024) void gemv_lds_kernel(
+// ALDS: the limbs of all b tokens are staged in LDS (one copy per workgroup);
+// otherwise each wave loads its A fragments from L2 into registers with its tiles.
+// Issue order per wave: direct loads into LDS (scale block, limbs), then for each
+// of the PMAX pairs its A fragments (if not ALDS) and its RB tiles.  The fences
+// keep that order, the wave waits only for the direct loads before the barrier,
+// and the compiler then waits for each pair's own loads right before its MFMAs,
+// so a pair is computed while later pairs are still arriving.  A wave with fewer
+// than PMAX pairs repeats its last pair with scale 0 (no branch around loads).
+// Variants that hold many tiles (and A fragments) in registers get 512-thread
+// workgroups, hence up to 256 VGPRs, instead of 1024 threads and 128 VGPRs.
+constexpr bool stream_heavy(bool alds, int rb, int pmax, bool lp) {
+  return alds ? pmax * rb > 10 : pmax * (rb + (lp ? 4 : 8)) > 16;
+}
+constexpr int stream_threads(bool alds, int rb, int pmax, bool lp) {
+  return stream_heavy(alds, rb, pmax, lp) ? 512 : 1024;
+}
+
+template <int RB, int NT, int PMAX, bool LP, bool ALDS>
+__global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_stream_kernel(
     const int8_t *__restrict__ limbs, const float *__restrict__ sigma, int b, int64_t K,
     int64_t Kp, int64_t N, const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
     void *__restrict__ y, int y_dtype, int lds_limb_bytes) {
+  constexpr int NA = LP ? 4 : 8;  // A fragment loads per pair when not ALDS
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int8_t *lx = reinterpret_cast<int8_t *>(smem);
-  float *red = reinterpret_cast<float *>(smem + lds_limb_bytes);
+  char *ls = smem + (ALDS ? lds_limb_bytes : 0);
+  const int G = int(K / kGroup);
+  float *red = reinterpret_cast<float *>(ls + scale_lds_bytes(16 * RB, G));
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15, qd = lane >> 4;
-  const int G = int(K / kGroup);
   const int GP = (G + 1) >> 1;
   const int64_t NB = (N + 15) >> 4;
   const int p_begin = (GP * wave) / W;
-  const int p_end = (GP * (wave + 1)) / W;
+  const int np = (GP * (wave + 1)) / W - p_begin;
   const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
 
-  // 1. every weight tile and scale pair this wave needs (at most PMAX pairs)
-  uint4 wv[PMAX][RB];
-  float sv[PMAX][2][RB];
-#pragma unroll
-  for (int pi = 0; pi < PMAX; ++pi) {
-    if (p_begin + pi < p_end) {
-      const int p = p_begin + pi;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int64_t rbg = min(int64_t(blockIdx.x) * RB + rb, NB - 1);
-        const int64_t n = n0 + 16 * rb + col;
-        const int64_t nn = n < N ? n : N - 1;
-        wv[pi][rb] = load_tile(packed, rbg, GP, p, lane);
-        load_pair_scales(scales + nn * G, G, p, sv[pi][0][rb], sv[pi][1][rb]);
-      }
+  // A operand row of this lane: (token, limb) per the LP or two-limb mapping
+  const int tok = LP ? lp_token(col) : token_of_arow(col);
+  const int tok_ld = tok < b ? tok : b - 1;
+  const int64_t arow = LP ? int64_t(col & 1) * b + tok_ld : tok_ld;
+  const int8_t *gah = limbs + arow * Kp + 32 * qd;      // global limb rows
+  const int8_t *gal = gah + int64_t(b) * Kp;
+  const int8_t *lah = lx + arow * Kp + 32 * qd;         // the same rows in LDS
+  const int8_t *lal = lah + int64_t(b) * Kp;
+
+  // 1. direct loads into LDS
+  stage_scales(scales, N, G, n0, 16 * RB, ls, wave, W, lane);
+  if (ALDS) {
+    for (int blk = wave; blk * 1024 < lds_limb_bytes; blk += W) {
+      const int64_t off = int64_t(blk) * 1024 + 16 * lane;
+      const int64_t src = off < 2 * int64_t(b) * Kp ? off : 0;
+      __builtin_amdgcn_global_load_lds(limbs + src,
+                                       (__attribute__((address_space(3))) void *)(lx + blk * 1024),
+                                       16, 0, 0);
     }
   }
-  // 2. limbs of all b tokens -> LDS, 1 KB per wave per step, straight from global
-  for (int blk = wave; blk * 1024 < lds_limb_bytes; blk += W) {
-    const int64_t off = int64_t(blk) * 1024 + 16 * lane;
-    const int64_t src = off < 2 * int64_t(b) * Kp ? off : 0;
-    __builtin_amdgcn_global_load_lds(limbs + src,
-                                     (__attribute__((address_space(3))) void *)(lx + blk * 1024), 16,
-                                     0, 0);
+  asm volatile("" ::: "memory");
+  // 2. register loads of every pair
+  v4i ga[ALDS ? 1 : PMAX][2][2][LP ? 1 : 2];  // [pair][group][64-k half][limb]
+  uint4 wv[PMAX][RB];
+#pragma unroll
+  for (int pi = 0; pi < PMAX; ++pi) {
+    const int p = p_begin + (pi < np ? pi : np - 1);
+    if (!ALDS) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int64_t gl = min(2 * p + gi, G - 1);  // a padded last group reads a valid row part
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ga[ALDS ? 0 : pi][gi][h][0] = *reinterpret_cast<const v4i *>(gah + 128 * gl + 16 * h);
+          if (!LP) ga[ALDS ? 0 : pi][gi][h][LP ? 0 : 1] = *reinterpret_cast<const v4i *>(gal + 128 * gl + 16 * h);
+        }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      wv[pi][rb] = load_tile(packed, min(int64_t(blockIdx.x) * RB + rb, NB - 1), GP, p, lane);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  asm volatile("" ::: "memory");
+  // 3. wait for the direct loads only; the register loads may stay in flight
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<PMAX * (RB + (ALDS ? 0 : NA))>());
+  __builtin_amdgcn_s_barrier();
 
-  // 3. compute
+  // 4. pairs in arrival order.  LDS is read through lds_read* so that the
+  //    compiler, which cannot tell these reads from the destinations of the
+  //    direct loads, does not make each of them wait for every register load.
   float acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[rb][i] = 0.0f;
-  const int tok = token_of_arow(col);
-  const int tok_ld = tok < b ? tok : b - 1;
-  const int8_t *lah = lx + int64_t(tok_ld) * Kp + 32 * qd;
-  const int8_t *lal = lah + int64_t(b) * Kp;
 #pragma unroll
   for (int pi = 0; pi < PMAX; ++pi) {
-    if (p_begin + pi < p_end) {
-      const int p = p_begin + pi;
-      v4i ah[2][2], al[2][2];
+    const bool live = pi < np;
+    const int p = p_begin + (live ? pi : np - 1);
+    v4i ah[2][2], al[2][2];
+    uint32_t sb[2][RB];
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        const int gl = min(2 * p + gi, G - 1);  // a padded last group reads a valid row part
+    for (int gi = 0; gi < 2; ++gi) {
+      const int gl = min(2 * p + gi, G - 1);
+      if (ALDS) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          ah[gi][h] = *reinterpret_cast<const v4i *>(lah + 128 * gl + 16 * h);
-          al[gi][h] = *reinterpret_cast<const v4i *>(lal + 128 * gl + 16 * h);
+          ah[gi][h] = lds_read16(lah + 128 * gl + 16 * h);
+          if (!LP) al[gi][h] = lds_read16(lal + 128 * gl + 16 * h);
         }
       }
-      pair_mfma<RB, NT>(ah, al, wv[pi], sv[pi], acc);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sb[gi][rb] = lds_read_u16(ls + 2 * ((16 * rb + col) * G + gl));
     }
+    lds_wait<RB>(ah, al, sb, LP || !ALDS);
+    if (!ALDS) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ah[gi][h] = ga[ALDS ? 0 : pi][gi][h][0];
+          al[gi][h] = ga[ALDS ? 0 : pi][gi][h][LP ? 0 : 1];
+        }
+    } else if (LP) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) al[gi][h] = ah[gi][h];
+    }
+    float sv[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      sv[0][rb] = live ? half_bits_to_float(uint16_t(sb[0][rb])) : 0.0f;
+      sv[1][rb] = live && 2 * p + 1 < G ? half_bits_to_float(uint16_t(sb[1][rb])) : 0.0f;
+    }
+    pair_mfma<RB, NT, LP>(ah, al, wv[pi], sv, acc);
   }
-  __syncthreads();  // every wave is done with the limbs before `red` is written
-  reduce_and_store<RB, NT>(acc, red, W, wave, lane, b, n0, N, sigma, y, y_dtype);
+  __syncthreads();  // every wave is done with LDS before `red` is written
+  reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, sigma, y, y_dtype);
 }
 
 // --------------------------------------------------------------------------
-// gemv_reg: limb fragments in registers, two pairs of groups in flight per wave
+// gemv_ring: limb fragments in registers, two pairs of groups in flight per wave
+// (for long K, where a wave's pairs do not all fit in registers at once)
 // --------------------------------------------------------------------------
 template <int RB>
 struct PairSlot {
   v4i ah[2][2], al[2][2];  // limbs: [group of the pair][64-k half]
   uint4 w[RB];             // tile words, per row block
-  float s[2][RB];          // group scales
 };
 
-template <int RB>
+template <int RB, bool LP>
 __device__ __forceinline__ void load_pair(PairSlot<RB> &f, int p, int G, int GP, const int8_t *ah,
                                           const int8_t *al, const uint32_t *__restrict__ packed,
-                                          const int64_t (&rbg)[RB], const uint16_t *const (&srow)[RB],
-                                          int lane) {
+                                          const int64_t (&rbg)[RB], int lane) {
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int gl = min(2 * p + gi, G - 1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f.ah[gi][h] = *reinterpret_cast<const v4i *>(ah + 128 * int64_t(gl) + 16 * h);
-      f.al[gi][h] = *reinterpret_cast<const v4i *>(al + 128 * int64_t(gl) + 16 * h);
+      if (!LP) f.al[gi][h] = *reinterpret_cast<const v4i *>(al + 128 * int64_t(gl) + 16 * h);
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    f.w[rb] = load_tile(packed, rbg[rb], GP, p, lane);
-    load_pair_scales(srow[rb], G, p, f.s[0][rb], f.s[1][rb]);
-  }
+  for (int rb = 0; rb < RB; ++rb) f.w[rb] = load_tile(packed, rbg[rb], GP, p, lane);
+}
+
+// scales of pair p for the lane's rows, from the staged block
+template <int RB>
+__device__ __forceinline__ void pair_scales(float (&s)[2][RB], const char *ls, int col, int G, int p) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) pair_scales_lds(ls, 16 * rb + col, G, p, s[0][rb], s[1][rb]);
 }
 
 // wave cap per workgroup: larger row tiles need more registers per wave
@@ -335,12 +479,14 @@ struct GemvWaveCap {
   static constexpr int value = RB == 1 ? 12 : RB == 2 ? 8 : 4;
 };
 
-template <int RB, int NT>
-__global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_reg_kernel(
+template <int RB, int NT, bool LP>
+__global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
     const int8_t *__restrict__ limbs, const float *__restrict__ sigma, int b, int64_t K,
     int64_t Kp, int64_t N, const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
     void *__restrict__ y, int y_dtype) {
-  extern __shared__ float red[];  // (W - 1) * RB * NT * 64 floats
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *ls = smem;  // scale block of the workgroup's rows, then (W - 1) * RB * NT * 64 floats
+  float *red = reinterpret_cast<float *>(smem + scale_lds_bytes(16 * RB, int(K / kGroup)));
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -352,18 +498,13 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_reg_kernel(
   const int p_end = (GP * (wave + 1)) / W;
   const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
 
-  const int tok = token_of_arow(col);
+  const int tok = LP ? lp_token(col) : token_of_arow(col);
   const int tok_ld = tok < b ? tok : b - 1;
-  const int8_t *ah = limbs + int64_t(tok_ld) * Kp + 32 * qd;
+  const int8_t *ah = limbs + int64_t(LP ? (col & 1) * b + tok_ld : tok_ld) * Kp + 32 * qd;
   const int8_t *al = ah + int64_t(b) * Kp;
   int64_t rbg[RB];
-  const uint16_t *srow[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    rbg[rb] = min(int64_t(blockIdx.x) * RB + rb, NB - 1);
-    const int64_t n = n0 + 16 * rb + col;
-    srow[rb] = scales + (n < N ? n : N - 1) * G;
-  }
+  for (int rb = 0; rb < RB; ++rb) rbg[rb] = min(int64_t(blockIdx.x) * RB + rb, NB - 1);
 
   float acc[RB][4];
 #pragma unroll
@@ -373,24 +514,30 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_reg_kernel(
 
   // two pair slots: slot (p - p_begin) % 2; the next pair is in flight while one is used
   PairSlot<RB> sl[2];
-  if (p_begin < p_end) load_pair<RB>(sl[0], p_begin, G, GP, ah, al, packed, rbg, srow, lane);
-  if (p_begin + 1 < p_end) load_pair<RB>(sl[1], p_begin + 1, G, GP, ah, al, packed, rbg, srow, lane);
+  if (p_begin < p_end) load_pair<RB, LP>(sl[0], p_begin, G, GP, ah, al, packed, rbg, lane);
+  if (p_begin + 1 < p_end) load_pair<RB, LP>(sl[1], p_begin + 1, G, GP, ah, al, packed, rbg, lane);
+  stage_scales(scales, N, G, n0, 16 * RB, ls, wave, W, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int p = p_begin; p < p_end; p += 2) {
-    pair_mfma<RB, NT>(sl[0].ah, sl[0].al, sl[0].w, sl[0].s, acc);
-    if (p + 2 < p_end) load_pair<RB>(sl[0], p + 2, G, GP, ah, al, packed, rbg, srow, lane);
+    float s[2][RB];
+    pair_scales<RB>(s, ls, col, G, p);
+    pair_mfma<RB, NT, LP>(sl[0].ah, LP ? sl[0].ah : sl[0].al, sl[0].w, s, acc);
+    if (p + 2 < p_end) load_pair<RB, LP>(sl[0], p + 2, G, GP, ah, al, packed, rbg, lane);
     if (p + 1 < p_end) {
-      pair_mfma<RB, NT>(sl[1].ah, sl[1].al, sl[1].w, sl[1].s, acc);
-      if (p + 3 < p_end) load_pair<RB>(sl[1], p + 3, G, GP, ah, al, packed, rbg, srow, lane);
+      pair_scales<RB>(s, ls, col, G, p + 1);
+      pair_mfma<RB, NT, LP>(sl[1].ah, LP ? sl[1].ah : sl[1].al, sl[1].w, s, acc);
+      if (p + 3 < p_end) load_pair<RB, LP>(sl[1], p + 3, G, GP, ah, al, packed, rbg, lane);
     }
   }
-  reduce_and_store<RB, NT>(acc, red, W, wave, lane, b, n0, N, sigma, y, y_dtype);
+  reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, sigma, y, y_dtype);
 }
 
 // --------------------------------------------------------------------------
 // variant choice and launch
 // --------------------------------------------------------------------------
 struct GemvPlan {
-  bool lds;
+  int kind;  // 0: stream with limbs in LDS, 1: stream with limbs from L2, 2: ring
   int rb, waves, pmax;
   int lds_limb_bytes;
   size_t lds_bytes;
@@ -398,79 +545,141 @@ struct GemvPlan {
 };
 
 constexpr int kLdsLimbBudget = 96 * 1024;
-constexpr int kPmax = 5;  // pairs per wave in the LDS kernel
+constexpr int kPmaxLds = 5;   // pairs per wave, limbs in LDS
+constexpr int kPmaxReg = 3;   // pairs per wave, A fragments in registers
+constexpr int kMaxWaves = 16;
+
+// Row blocks per workgroup: the smallest of 1, 2, 4 whose workgroups all fit on
+// the chip at once (one round), given how many fit per compute unit by LDS and
+// by waves; 4 when none does.
+constexpr int kCUs = 256;
+constexpr int kLdsPerCU = 160 * 1024;
+constexpr int kWavesPerCU = 32;
+
+int fit_rb(int64_t N, size_t lds_fixed, size_t lds_per_rb, int waves) {
+  for (int rb = 1; rb <= 4; rb *= 2) {
+    const size_t lds = lds_fixed + lds_per_rb * rb;
+    const int64_t per_cu = std::min<int64_t>(int64_t(kLdsPerCU / lds), kWavesPerCU / waves);
+    if ((N + 16 * rb - 1) / (16 * rb) <= per_cu * kCUs) return rb;
+  }
+  return 4;
+}
 
 GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   const int64_t G = K / kGroup, GP = (G + 1) / 2;
   const int64_t Kp = K + kRowPad;
-  const int nt = int((b + 3) / 4);
-  GemvPlan p{};
+  const int nt = b <= 8 ? 2 : int((b + 3) / 4);  // accumulators per row block and lane
   const int64_t limb_bytes = (2 * b * Kp + 1023) / 1024 * 1024;
-  if (limb_bytes <= kLdsLimbBudget && GP <= 16 * kPmax) {
-    p.lds = true;
-    p.waves = int(GP < 10 ? GP : (GP + 1) / 2 < 16 ? (GP + 1) / 2 : 16);
-    p.pmax = int((GP + p.waves - 1) / p.waves);
-    p.rb = N >= 16 * 2 * 512 ? 2 : 1;
+  GemvPlan p{};
+  const bool lp = b <= 8;
+  // waves for PMAX pairs each, within the wave cap of the resulting variant
+  auto shape = [&](bool alds, int rb, int pmax) {
+    for (;; ++pmax) {
+      const int cap = stream_heavy(alds, rb, pmax, lp) ? 8 : kMaxWaves;
+      const int waves = int((GP + pmax - 1) / pmax);
+      if (waves <= cap || pmax >= (alds ? kPmaxLds : kPmaxReg)) {
+        p.waves = waves;
+        p.pmax = int((GP + waves - 1) / waves);
+        return;
+      }
+    }
+  };
+  if (limb_bytes <= kLdsLimbBudget && GP <= 8 * kPmaxLds) {
+    // limbs in LDS.  Small batches: few waves with several pairs each, so that
+    // pairs are computed while later ones arrive; b > 4: up to four row blocks
+    // share one copy of the limbs.
+    p.kind = 0;
     p.lds_limb_bytes = int(limb_bytes);
-    p.lds_bytes = size_t(limb_bytes) + size_t(p.waves - 1) * p.rb * nt * 64 * sizeof(float);
-    static const char *names[2] = {"gemv_lds_rb1", "gemv_lds_rb2"};
-    p.name = names[p.rb - 1];
-    return p;
+    shape(true, 1, b <= 2 ? 4 : b <= 4 ? 5 : 2);
+    p.rb = fit_rb(N, size_t(limb_bytes), scale_lds_bytes(16, int(G)) + size_t(p.waves) * nt * 256,
+                  p.waves);
+    if (b <= 4) p.rb = std::min(p.rb, 2);
+    shape(true, p.rb, p.pmax);
+  } else if (GP <= 8 * kPmaxReg) {
+    // limbs from L2 into registers, all pairs at once
+    p.kind = 1;
+    p.lds_limb_bytes = 0;
+    p.rb = (N + 63) / 64 >= 128 ? 4 : (N + 31) / 32 >= 128 ? 2 : 1;  // A fragments serve RB tiles
+    shape(false, p.rb, 2);
+  } else {
+    p.kind = 2;
+    p.rb = N >= 16 * 2 * 128 ? 2 : 1;
+    const int cap = p.rb == 1 ? GemvWaveCap<1>::value : GemvWaveCap<2>::value;
+    p.waves = int(GP < cap ? GP : cap);
+    p.pmax = 0;
+    p.lds_limb_bytes = 0;
   }
-  p.lds = false;
-  p.rb = N >= 16 * 2 * 128 ? 2 : 1;
-  const int cap = p.rb == 1 ? GemvWaveCap<1>::value : GemvWaveCap<2>::value;
-  p.waves = int(GP < cap ? GP : cap);
-  p.lds_bytes = size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * nt * 64 * sizeof(float);
-  static const char *names[2] = {"gemv_reg_rb1", "gemv_reg_rb2"};
-  p.name = names[p.rb - 1];
+  p.lds_bytes = size_t(p.lds_limb_bytes) + scale_lds_bytes(16 * p.rb, int(G)) +
+                size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * nt * 64 * sizeof(float);
+  static const char *names[3][3] = {{"gemv_stream_lds_rb1", "gemv_stream_lds_rb2", "gemv_stream_lds_rb4"},
+                                    {"gemv_stream_reg_rb1", "gemv_stream_reg_rb2", "gemv_stream_reg_rb4"},
+                                    {"gemv_ring_rb1", "gemv_ring_rb2", "gemv_ring_rb2"}};
+  p.name = names[p.kind][p.rb == 4 ? 2 : p.rb - 1];
   return p;
 }
 
-template <int RB, int NT, int PMAX>
-void launch_lds_t(const GemvPlan &p, dim3 grid, const GemvWs &w, int64_t b, int64_t K, int64_t N,
-                  const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
-                  hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_lds_kernel<RB, NT, PMAX>), grid, dim3(64 * p.waves), p.lds_bytes, stream,
-                     w.xhi, w.sigma, int(b), K, w.Kp, N, packed, scales, y, y_dtype,
-                     p.lds_limb_bytes);
+struct GemvArgs {
+  const GemvWs *w;
+  int64_t b, K, N;
+  const uint32_t *packed;
+  const uint16_t *scales;
+  void *y;
+  int y_dtype;
+  hipStream_t stream;
+};
+
+template <int RB, int NT, int PMAX, bool LP, bool ALDS>
+void launch_stream_t(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
+  hipLaunchKernelGGL((gemv_stream_kernel<RB, NT, PMAX, LP, ALDS>), grid, dim3(64 * p.waves), p.lds_bytes,
+                     a.stream, a.w->xhi, a.w->sigma, int(a.b), a.K, a.w->Kp, a.N, a.packed, a.scales, a.y,
+                     a.y_dtype, p.lds_limb_bytes);
 }
 
-template <int RB, int NT>
-void launch_lds_rn(const GemvPlan &p, dim3 grid, const GemvWs &w, int64_t b, int64_t K, int64_t N,
-                   const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
-                   hipStream_t stream) {
-  switch (p.pmax) {
-    case 1: launch_lds_t<RB, NT, 1>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    case 2: launch_lds_t<RB, NT, 2>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    case 3: launch_lds_t<RB, NT, 3>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    case 4: launch_lds_t<RB, NT, 4>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    default: launch_lds_t<RB, NT, 5>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
+template <int RB, int NT, bool LP, bool ALDS>
+void launch_stream_p(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
+  if constexpr (ALDS) {
+    switch (p.pmax) {
+      case 1: launch_stream_t<RB, NT, 1, LP, ALDS>(p, grid, a); break;
+      case 2: launch_stream_t<RB, NT, 2, LP, ALDS>(p, grid, a); break;
+      case 3: launch_stream_t<RB, NT, 3, LP, ALDS>(p, grid, a); break;
+      case 4: launch_stream_t<RB, NT, 4, LP, ALDS>(p, grid, a); break;
+      default: launch_stream_t<RB, NT, 5, LP, ALDS>(p, grid, a); break;
+    }
+  } else {
+    switch (p.pmax) {
+      case 1: launch_stream_t<RB, NT, 1, LP, ALDS>(p, grid, a); break;
+      case 2: launch_stream_t<RB, NT, 2, LP, ALDS>(p, grid, a); break;
+      default: launch_stream_t<RB, NT, 3, LP, ALDS>(p, grid, a); break;
+    }
   }
 }
 
-template <int RB>
-void launch_lds_r(const GemvPlan &p, dim3 grid, const GemvWs &w, int64_t b, int64_t K, int64_t N,
-                  const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
-                  hipStream_t stream) {
-  switch ((b + 3) / 4) {
-    case 1: launch_lds_rn<RB, 1>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    case 2: launch_lds_rn<RB, 2>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    case 3: launch_lds_rn<RB, 3>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
-    default: launch_lds_rn<RB, 4>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream); break;
+template <int RB, bool ALDS>
+void launch_stream_n(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
+  switch ((a.b + 3) / 4) {
+    case 1:
+    case 2: launch_stream_p<RB, 2, true, ALDS>(p, grid, a); break;
+    case 3: launch_stream_p<RB, 3, false, ALDS>(p, grid, a); break;
+    default: launch_stream_p<RB, 4, false, ALDS>(p, grid, a); break;
   }
 }
 
+template <bool ALDS>
+void launch_stream(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
+  if (p.rb == 4) launch_stream_n<4, ALDS>(p, grid, a);
+  else if (p.rb == 2) launch_stream_n<2, ALDS>(p, grid, a);
+  else launch_stream_n<1, ALDS>(p, grid, a);
+}
+
 template <int RB>
-void launch_reg_r(const GemvPlan &p, dim3 grid, const GemvWs &w, int64_t b, int64_t K, int64_t N,
-                  const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
-                  hipStream_t stream) {
+void launch_ring_r(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
   const dim3 blk(64 * p.waves);
-  switch ((b + 3) / 4) {
-    case 1: hipLaunchKernelGGL((gemv_reg_kernel<RB, 1>), grid, blk, p.lds_bytes, stream, w.xhi, w.sigma, int(b), K, w.Kp, N, packed, scales, y, y_dtype); break;
-    case 2: hipLaunchKernelGGL((gemv_reg_kernel<RB, 2>), grid, blk, p.lds_bytes, stream, w.xhi, w.sigma, int(b), K, w.Kp, N, packed, scales, y, y_dtype); break;
-    case 3: hipLaunchKernelGGL((gemv_reg_kernel<RB, 3>), grid, blk, p.lds_bytes, stream, w.xhi, w.sigma, int(b), K, w.Kp, N, packed, scales, y, y_dtype); break;
-    default: hipLaunchKernelGGL((gemv_reg_kernel<RB, 4>), grid, blk, p.lds_bytes, stream, w.xhi, w.sigma, int(b), K, w.Kp, N, packed, scales, y, y_dtype); break;
+  const GemvWs &w = *a.w;
+  switch ((a.b + 3) / 4) {
+    case 1:
+    case 2: hipLaunchKernelGGL((gemv_ring_kernel<RB, 2, true>), grid, blk, p.lds_bytes, a.stream, w.xhi, w.sigma, int(a.b), a.K, w.Kp, a.N, a.packed, a.scales, a.y, a.y_dtype); break;
+    case 3: hipLaunchKernelGGL((gemv_ring_kernel<RB, 3, false>), grid, blk, p.lds_bytes, a.stream, w.xhi, w.sigma, int(a.b), a.K, w.Kp, a.N, a.packed, a.scales, a.y, a.y_dtype); break;
+    default: hipLaunchKernelGGL((gemv_ring_kernel<RB, 4, false>), grid, blk, p.lds_bytes, a.stream, w.xhi, w.sigma, int(a.b), a.K, w.Kp, a.N, a.packed, a.scales, a.y, a.y_dtype); break;
   }
 }
 
@@ -497,14 +706,12 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
   const GemvWs w = carve(const_cast<void *>(workspace), b, K);
   const GemvPlan p = plan_gemv(b, K, N);
   const dim3 grid(unsigned((N + 16 * p.rb - 1) / (16 * p.rb)));
+  const GemvArgs a{&w, b, K, N, packed, scales, y, y_dtype, stream};
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  if (p.lds) {
-    if (p.rb == 2) launch_lds_r<2>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream);
-    else launch_lds_r<1>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream);
-  } else {
-    if (p.rb == 2) launch_reg_r<2>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream);
-    else launch_reg_r<1>(p, grid, w, b, K, N, packed, scales, y, y_dtype, stream);
-  }
+  if (p.kind == 0) launch_stream<true>(p, grid, a);
+  else if (p.kind == 1) launch_stream<false>(p, grid, a);
+  else if (p.rb == 2) launch_ring_r<2>(p, grid, a);
+  else launch_ring_r<1>(p, grid, a);
   set_last_kernel(p.name);
   return hipGetLastError();
 }
