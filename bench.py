@@ -118,7 +118,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
            "sources": {k: source_hash(k) for k in KERNEL_SOURCES}, "gemv": {}, "gemm": {}}
     for counter, path, fac in (("fetch", fetch_csv, f_fac), ("write", write_csv, w_fac)):
         rows = _pmc_rows(path)
-        gemv = [(n, v) for n, v in rows if "gemv_lds_kernel" in n or "gemv_reg_kernel" in n]
+        gemv = [(n, v) for n, v in rows if "gemv_stream_kernel" in n or "gemv_ring_kernel" in n]
         gemm = [(n, v) for n, v in rows if "gemm_i8_kernel" in n]
         if not gemv or len(gemv) % (DEC_LAYERS * len(DECODE_BS)) or not gemm or len(gemm) % (2 * PRE_LAYERS):
             raise SystemExit(f"unexpected launch counts in {path}: {len(gemv)} GEMV, {len(gemm)} GEMM")
