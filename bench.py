@@ -65,6 +65,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-stack", action="store_true", help="skip the 64-block whole-stack pass")
+    p.add_argument("--stack-steps", type=int, default=5)
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -319,6 +321,13 @@ def main():
             pre_out[k]["traffic_bytes"] = traffic["gemm"][k]["traffic_bytes"]
         gemm_traffic = round(float(np.mean([traffic["gemm"][k]["traffic_bytes"] for k in pre_out])))
 
+    stack = None
+    if not args.no_stack:
+        del qkv, gate_up, down, pre
+        torch.cuda.empty_cache()
+        log("stack64: packing 256 layers")
+        stack = stack_pass(tl, torch, dev, args.stack_steps, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle decode qkv b=16")
@@ -351,9 +360,103 @@ def main():
                      "kernel": "GEMV weight stream (" + ", ".join(sorted({v["kernel"] for v in by_b.values()})) + ")"},
         "roofline_prefill": {"bound": "mfma", "achieved": round(pre_tops, 1), "peak": INT8_PEAK_TOPS,
                              "unit": "TOP/s", "frac": round(pre_tops / INT8_PEAK_TOPS, 4), "traffic": gemm_traffic},
+        "stack64": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def stack_pass(tl, torch, dev, steps, log):
+    """64 synthetic decoder blocks x (qkv, o, gate_up, down), weights resident in HBM.
+
+    One activation tensor per layer type is shared by the 64 blocks (the layers do
+    not chain).  Decode pass: per type, rotation + GEMV prep once, then the 64
+    GEMVs (b = 16).  Prefill pass: per type, rotation + quantisation of a
+    2048-token chunk once, then the 64 GEMMs.  Reported: GB/s of the GEMV launches
+    and TOP/s of the GEMM launches (events around each type's 64 launches), and
+    the whole-pass times.
+    """
+    import synth
+    types = [(name, K, N) for name, K, N in synth.CONFIGS[4]["layers"]]
+    blocks = synth.CONFIGS[4]["blocks"]
+    layers = []
+    packed_bytes = 0
+    for blk in range(blocks):
+        for ti, (name, K, N) in enumerate(types):
+            L = synth.LayerInputs(0, 4, 4 * blk + ti, K, N)
+            codes = L.codes_torch(dev)
+            scales = torch.from_numpy(L.scales()).to(dev)
+            packed, q, rs = tl.pack_weights(codes, scales)
+            del codes
+            layers.append((ti, packed, scales, q, rs))
+            packed_bytes += packed.numel() * 4 + scales.numel() * 2 + q.numel() + rs.numel() * 4
+    torch.cuda.synchronize()
+    bf16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    B, M = 16, 2048
+    io = []
+    for ti, (name, K, N) in enumerate(types):
+        io.append(dict(K=K, N=N, xd=bf16(synth.activations(0, 4, ti, B, K)),
+                       xp=bf16(synth.activations(0, 4, len(types) + ti, M, K)),
+                       xr=torch.empty((B, K), dtype=torch.float32, device=dev),
+                       ws=torch.empty((tl.gemv_workspace_size(B, K, N),), dtype=torch.uint8, device=dev),
+                       yd=torch.empty((B, N), dtype=torch.bfloat16, device=dev),
+                       xrp=torch.empty((M, K), dtype=torch.float32, device=dev),
+                       xq=torch.empty((M, K), dtype=torch.int8, device=dev),
+                       sx=torch.empty((M,), dtype=torch.float32, device=dev),
+                       yp=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def decode(rec):
+        for ti, P in enumerate(io):
+            tl.hadamard_blk(P["xd"], out=P["xr"])
+            tl.gemv_prepare(P["xr"], P["ws"])
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for lt, packed, scales, q, rs in layers:
+                if lt == ti:
+                    tl.gemv_prepared(P["ws"], B, P["K"], packed, scales, P["yd"])
+            e1.record(stream)
+            rec.append((e0, e1))
+
+    def prefill(rec):
+        for ti, P in enumerate(io):
+            tl.hadamard_blk(P["xp"], out=P["xrp"])
+            tl.quant_act_int8(P["xrp"], P["xq"], P["sx"])
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            for lt, packed, scales, q, rs in layers:
+                if lt == ti:
+                    tl.gemm_int8_rescale(P["xq"], P["sx"], packed, q, rs, out=P["yp"])
+            e1.record(stream)
+            rec.append((e0, e1))
+
+    out = {"blocks": blocks, "layers": len(layers), "weight_bytes": packed_bytes}
+    for name, fn in (("decode_b16", decode), ("prefill_m2048", prefill)):
+        fn([])
+        torch.cuda.synchronize()
+        rec = []
+        t0, t1 = ev(), ev()
+        t0.record(stream)
+        for _ in range(steps):
+            fn(rec)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        kern_s = sum(a.elapsed_time(b) for a, b in rec) / steps * 1e-3
+        pass_ms = t0.elapsed_time(t1) / steps
+        if name == "decode_b16":
+            nbytes = sum(P["N"] * P["K"] // 4 + P["N"] * (P["K"] // 128) * 2 + 2 * B * P["K"] + 2 * B * P["N"]
+                         for ti, P in enumerate(io) for lt, *_ in layers if lt == ti)
+            out[name] = {"gemv_GBps": round(nbytes / kern_s / 1e9, 1), "gemv_ms": round(kern_s * 1e3, 3),
+                         "pass_ms": round(pass_ms, 3), "bytes": nbytes,
+                         "frac": round(nbytes / kern_s / 1e9 / HBM_PEAK_GBS, 4)}
+        else:
+            ops = sum(2.0 * M * P["K"] * P["N"] for ti, P in enumerate(io) for lt, *_ in layers if lt == ti)
+            out[name] = {"gemm_TOPs": round(ops / kern_s / 1e12, 1), "gemm_ms": round(kern_s * 1e3, 3),
+                         "pass_ms": round(pass_ms, 3), "ops": ops,
+                         "frac": round(ops / kern_s / 1e12 / INT8_PEAK_TOPS, 4)}
+        log(f"stack64 {name}: {out[name]}")
+    return out
 
 
 def cpu_baseline(seconds):

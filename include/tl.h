@@ -192,11 +192,13 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
  * out acc_out    int32  [M, N] or NULL: acc[m,n] = sum_k xq[m,k] code[n,k] q[n,k/128]
  *                (exact; |acc| <= K * 127^2, so K <= 133143 keeps it in int32)
  * workspace      device scratch of at least tl_gemm_workspace_size(M, K, N)
- *                bytes (may be NULL when that size is 0).  It holds the int32
- *                partial tiles of K-split work and one counter per split tile.
- *                It must be zero-filled before its first use; every call leaves
- *                its counters at zero again, so it can be reused without
- *                clearing.  Calls that overlap in time must not share one.
+ *                bytes (may be NULL when that size is 0).  Layout: 256 int32
+ *                counters (one per K-split tile; at most 255 are ever used),
+ *                then the int32 partial tiles of the K-split work.  It must be
+ *                zero-filled before its first use; every call leaves the
+ *                counters at zero again, so one workspace can be reused, also
+ *                across shapes, without clearing.  Calls that overlap in time
+ *                must not share one.
  * The size depends only on (M, K, N): the schedule is fixed for the 256
  * compute units of gfx950 (whole rounds of 128 x 256 tiles, the left-over
  * tiles split along K).

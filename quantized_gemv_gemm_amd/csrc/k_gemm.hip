@@ -421,7 +421,10 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   }
 }
 
-constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+// Workspace layout, the same for every shape so that one workspace serves calls
+// of different shapes: kSlots int32 counters (one per possible left-over tile;
+// fewer than kSlots tiles are ever left over), then the int32 partial tiles.
+constexpr size_t kCounterBytes = kSlots * sizeof(int32_t);
 
 }  // namespace
 
@@ -429,7 +432,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   const Schedule s = make_schedule(M, N, (K / kGroup + 1) / 2);
   if (s.split <= 1) return 0;
-  return align256(size_t(s.left()) * 4) + size_t(s.left() * s.split) * kTileInts * 4;
+  return kCounterBytes + size_t(s.left() * s.split) * kTileInts * 4;
 }
 
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
@@ -440,7 +443,7 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
   int32_t *counters = nullptr, *part = nullptr;
   if (s.split > 1) {
     counters = static_cast<int32_t *>(workspace);
-    part = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + align256(size_t(s.left()) * 4));
+    part = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
   }
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,

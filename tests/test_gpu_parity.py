@@ -305,6 +305,42 @@ def test_gemm_ragged(tl, M, K, N):
     _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "ragged")
 
 
+def test_gemm_workspace_reused_across_shapes(tl):
+    """One workspace, K-split GEMMs of different shapes in turn (64 and 128 split
+    tiles): the counters of one shape never overlap the partials of another, and
+    every call leaves them at zero."""
+    import torch
+    d = dev()
+    rng = np.random.default_rng(2048)
+    K, M = 5120, 2048
+    shapes = [5120, 10240, 5120]
+    layers = {}
+    for N in sorted(set(shapes)):
+        codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+        scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+        packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+        layers[N] = (codes, scales, packed, q, rs)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.exp(rng.standard_normal(M)).astype(np.float32)
+    xq_d, sx_d = to_dev(xq, d), to_dev(sx, d)
+    need = max(tl.gemm_workspace_size(M, K, N) for N in shapes)
+    assert all(tl.gemm_workspace_size(M, K, N) > 0 for N in shapes)
+    ws = torch.zeros((need,), dtype=torch.uint8, device=d)
+    toks = np.sort(rng.choice(M, 48, replace=False))
+    for N in shapes:
+        announce(f"gemm workspace reuse M={M} K={K} N={N}")
+        codes, scales, packed, q, rs = layers[N]
+        acc = poison_(torch.empty((M, N), dtype=torch.int32, device=d))
+        tl.gemm_int8_rescale(xq_d, sx_d, packed, q, rs, out_dtype=torch.float32, acc_out=acc, workspace=ws)
+        torch.cuda.synchronize()
+        rows = np.sort(rng.choice(N, 96, replace=False))
+        q_ref, _, _ = oracle.decompose_scales(scales[rows])
+        acc_ref = oracle.gemm_int8_acc(xq[toks], codes[rows], q_ref)
+        got = acc[torch.from_numpy(toks).to(d)][:, torch.from_numpy(rows).to(d)].cpu().numpy()
+        np.testing.assert_array_equal(got.astype(np.int64), acc_ref)
+        assert int(ws[:1024].view(torch.int32).abs().sum()) == 0   # counters back at zero
+
+
 def test_gemm_extreme_accumulator(tl):
     """All +-127 inputs and weights: |acc| = K * 127^2 at K = 17408 stays exact."""
     d = dev()
