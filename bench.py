@@ -1,12 +1,12 @@
 """Benchmark of the ternary linear layer on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  decode  for b = 1, 4, 8 and 16 tokens: block rotation -> GEMV activation prep
-          -> the GEMV weight stream of DEC_LAYERS qkv-shaped layers
-          (K=5120 -> N=10240, each a different weight copy);
+  decode  for b = 1, 4, 8 and 16 tokens: block rotation fused with the GEMV
+          activation prep (one kernel) -> the GEMV weight stream of DEC_LAYERS
+          qkv-shaped layers (K=5120 -> N=10240, each a different weight copy);
   prefill (512-token chunk): for gate_up (5120 -> 34816) and down (17408 -> 5120),
-          block rotation -> per-token int8 quantisation -> int8 GEMM + rescale of
-          PRE_LAYERS layers each.
+          block rotation fused with per-token int8 quantisation (one kernel) ->
+          int8 GEMM + rescale of PRE_LAYERS layers each.
 Weights are packed once (load time, not timed) and cloned into rotating copies
 (>= 1 GiB per layer type) so that successive launches read weights that are not
 resident in the 256 MB Infinity Cache.
@@ -212,7 +212,6 @@ def main():
 
     Kq, Nq = 5120, 10240
     x_dec = {b: bf16(synth.activations(0, 1, 0, b, Kq)) for b in DECODE_BS}
-    xr_dec = {b: torch.empty((b, Kq), dtype=torch.float32, device=dev) for b in DECODE_BS}
     ws_dec = {b: torch.empty((tl.gemv_workspace_size(b, Kq, Nq),), dtype=torch.uint8, device=dev)
               for b in DECODE_BS}
     y_dec = {b: torch.empty((b, Nq), dtype=torch.bfloat16, device=dev) for b in DECODE_BS}
@@ -221,7 +220,6 @@ def main():
     for name, copies, li, K, N in (("gate_up", gate_up, 0, 5120, 34816), ("down", down, 1, 17408, 5120)):
         pre[name] = dict(copies=copies, K=K, N=N,
                          x=bf16(synth.activations(0, 3, li, PREFILL_M, K)),
-                         xr=torch.empty((PREFILL_M, K), dtype=torch.float32, device=dev),
                          xq=torch.empty((PREFILL_M, K), dtype=torch.int8, device=dev),
                          sx=torch.empty((PREFILL_M,), dtype=torch.float32, device=dev),
                          y=torch.empty((PREFILL_M, N), dtype=torch.bfloat16, device=dev))
@@ -237,8 +235,7 @@ def main():
     def step(rec):
         """One pass of the hot path; appends (kind, key, n_launches, start, end) when rec is a list."""
         for b in DECODE_BS:
-            tl.hadamard_blk(x_dec[b], out=xr_dec[b])
-            tl.gemv_prepare(xr_dec[b], ws_dec[b])
+            tl.gemv_prepare_x(x_dec[b], ws_dec[b])          # rotation fused into the GEMV prep
             if rec is not None:
                 e0, e1 = ev(), ev()
                 e0.record(stream)
@@ -252,8 +249,7 @@ def main():
                 rec.append(("gemv", b, DEC_LAYERS, e0, e1))
         for name in ("gate_up", "down"):
             P = pre[name]
-            tl.hadamard_blk(P["x"], out=P["xr"])
-            tl.quant_act_int8(P["xr"], P["xq"], P["sx"])
+            tl.quant_act_int8_x(P["x"], xq=P["xq"], tok_scale=P["sx"])   # rotation fused into the quantisation
             if rec is not None:
                 e0, e1 = ev(), ev()
                 e0.record(stream)
@@ -271,6 +267,11 @@ def main():
         step(None)
     torch.cuda.synchronize()
 
+    # the timed region runs with Python's garbage collector off: a collection
+    # pause stalls the launch thread and shows up as idle GPU time in the events
+    import gc
+    gc.collect()
+    gc.disable()
     log(f"timing {args.steps} steps")
     rec = []
     t0, t1 = ev(), ev()
@@ -284,9 +285,28 @@ def main():
 
     gemv_ms = {b: [] for b in DECODE_BS}
     gemm_ms = {"gate_up": [], "down": []}
+    sink = {"gemv": gemv_ms, "gemm": gemm_ms}
     for kind, key, n, e0, e1 in rec:
-        (gemv_ms if kind == "gemv" else gemm_ms)[key].append(e0.elapsed_time(e1) / n)
+        sink[kind][key].append(e0.elapsed_time(e1) / n)
 
+    # the fused input kernels, each timed over a back-to-back run of its own
+    def run_time(fn, n=20):
+        fn()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+    prep_ms = {b: [run_time(lambda: tl.gemv_prepare_x(x_dec[b], ws_dec[b]))] for b in DECODE_BS}
+    quant_ms = {k: [run_time(lambda: tl.quant_act_int8_x(P["x"], xq=P["xq"], tok_scale=P["sx"]))]
+                for k, P in pre.items()}
+    gc.enable()
+
+    if os.environ.get("BENCH_DEBUG"):
+        for k, v in gemm_ms.items():
+            log(f"per-step ms {k}: {[round(x, 4) for x in v]}")
     by_b = {}
     tot_bytes = tot_s = 0.0
     for b in DECODE_BS:
@@ -352,6 +372,9 @@ def main():
                    "decode_b": list(DECODE_BS), "prefill_tokens": PREFILL_M,
                    "rotating_weight_bytes": ROTATE_BYTES},
         "decode_gemv_by_b": by_b,
+        "input_kernels_us": {
+            "decode_rotate_prep": {str(b): round(float(np.mean(prep_ms[b])) * 1e3, 2) for b in DECODE_BS},
+            "prefill_rotate_quant_m512": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in quant_ms.items()}},
         "prefill_tops": round(pre_tops, 1),
         "prefill_gemm": pre_out,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -397,10 +420,8 @@ def stack_pass(tl, torch, dev, steps, log):
     for ti, (name, K, N) in enumerate(types):
         io.append(dict(K=K, N=N, xd=bf16(synth.activations(0, 4, ti, B, K)),
                        xp=bf16(synth.activations(0, 4, len(types) + ti, M, K)),
-                       xr=torch.empty((B, K), dtype=torch.float32, device=dev),
                        ws=torch.empty((tl.gemv_workspace_size(B, K, N),), dtype=torch.uint8, device=dev),
                        yd=torch.empty((B, N), dtype=torch.bfloat16, device=dev),
-                       xrp=torch.empty((M, K), dtype=torch.float32, device=dev),
                        xq=torch.empty((M, K), dtype=torch.int8, device=dev),
                        sx=torch.empty((M,), dtype=torch.float32, device=dev),
                        yp=torch.empty((M, N), dtype=torch.bfloat16, device=dev)))
@@ -409,8 +430,7 @@ def stack_pass(tl, torch, dev, steps, log):
 
     def decode(rec):
         for ti, P in enumerate(io):
-            tl.hadamard_blk(P["xd"], out=P["xr"])
-            tl.gemv_prepare(P["xr"], P["ws"])
+            tl.gemv_prepare_x(P["xd"], P["ws"])
             e0, e1 = ev(), ev()
             e0.record(stream)
             for lt, packed, scales, q, rs in layers:
@@ -421,8 +441,7 @@ def stack_pass(tl, torch, dev, steps, log):
 
     def prefill(rec):
         for ti, P in enumerate(io):
-            tl.hadamard_blk(P["xp"], out=P["xrp"])
-            tl.quant_act_int8(P["xrp"], P["xq"], P["sx"])
+            tl.quant_act_int8_x(P["xp"], xq=P["xq"], tok_scale=P["sx"])
             e0, e1 = ev(), ev()
             e0.record(stream)
             for lt, packed, scales, q, rs in layers:
@@ -432,6 +451,9 @@ def stack_pass(tl, torch, dev, steps, log):
             rec.append((e0, e1))
 
     out = {"blocks": blocks, "layers": len(layers), "weight_bytes": packed_bytes}
+    import gc
+    gc.collect()
+    gc.disable()
     for name, fn in (("decode_b16", decode), ("prefill_m2048", prefill)):
         fn([])
         torch.cuda.synchronize()
@@ -456,6 +478,7 @@ def stack_pass(tl, torch, dev, steps, log):
                          "pass_ms": round(pass_ms, 3), "ops": ops,
                          "frac": round(ops / kern_s / 1e12 / INT8_PEAK_TOPS, 4)}
         log(f"stack64 {name}: {out[name]}")
+    gc.enable()
     return out
 
 

@@ -180,6 +180,26 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
                       void *stream);
 
 /*
+ * Fused layer inputs: the block rotation and the step that consumes it in one
+ * launch, so the rotated activations are never written to memory.
+ *   [P1] "前提" (rotation of the input), "4. 効いた高速化" (int8 per token after
+ *   the rotation).  Outputs are bit-identical to the unfused sequences:
+ *     tl_gemv_prepare_x   == tl_hadamard_blk then tl_gemv_prepare
+ *     tl_gemv_ternary_x   == tl_hadamard_blk then tl_gemv_ternary
+ *     tl_quant_act_int8_x == tl_hadamard_blk then tl_quant_act_int8
+ * in  x       bf16 [b or T, K] raw layer input; signs as in tl_hadamard_blk.
+ * Requires K % 1024 == 0 and K <= 65536 (TL_ERR_UNSUPPORTED above: use the
+ * unfused calls); other arguments as in the unfused entry points.
+ */
+int tl_gemv_prepare_x(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int tl_gemv_ternary_x(const uint16_t *x, int64_t b, int64_t K, int64_t N, const int8_t *signs,
+                      const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, int8_t *xq,
+                        float *tok_scale, void *stream);
+
+/*
  * tl_gemm_int8_rescale -- prefill int8 GEMM and rescale.
  *   [P1] "4. 効いた高速化" (W_int8 = code * q exactly in int8; one int8 GEMM,
  *   then a per-row and per-token rescale).

@@ -42,6 +42,10 @@ _SIGS = {
     "tl_gemv_prepared": (ctypes.c_int, [_c_p, _c_sz, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_int,
                                         _c_p]),
     "tl_quant_act_int8": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "tl_gemv_prepare_x": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_sz, _c_p]),
+    "tl_gemv_ternary_x": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, ctypes.c_int,
+                                         _c_p, _c_sz, _c_p]),
+    "tl_quant_act_int8_x": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p]),
     "tl_gemm_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "tl_gemm_int8_rescale": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
                                             ctypes.c_int, _c_p, _c_p, _c_sz, _c_p]),
@@ -171,6 +175,70 @@ def hadamard_blk(x, signs=None, out=None):
         raise ValueError("out must be [T, K]")
     _check("tl_hadamard_blk", lib().tl_hadamard_blk(_ptr(x), T, K, _ptr(signs), _ptr(out), _stream(x.device)))
     return out
+
+
+def _check_x(x, signs):
+    import torch
+    _need(x, "x", torch.bfloat16, 2)
+    if signs is not None:
+        _need(signs, "signs", torch.int8, 1)
+        if signs.shape != (x.shape[1],):
+            raise ValueError("signs must be [K]")
+
+
+def gemv_prepare_x(x, workspace, signs=None):
+    """Fused rotation + GEMV prep: limbs of the rotated x bf16 [b,K] into ``workspace``
+    (bit-identical to gemv_prepare(hadamard_blk(x, signs)))."""
+    import torch
+    _check_x(x, signs)
+    _need(workspace, "workspace", torch.uint8, 1)
+    b, K = x.shape
+    _check("tl_gemv_prepare_x", lib().tl_gemv_prepare_x(_ptr(x), b, K, _ptr(signs), _ptr(workspace),
+                                                        workspace.numel(), _stream(x.device)))
+    return workspace
+
+
+def gemv_ternary_x(x, packed, scales, signs=None, out_dtype=None, out=None, workspace=None):
+    """Decode layer from the raw input: x bf16 [b,K] -> y [b,N] (rotation fused into the prep)."""
+    import torch
+    _check_x(x, signs)
+    _need(scales, "scales", torch.float16, 2)
+    b, K = x.shape
+    N = scales.shape[0]
+    _check_packed(packed, N, K)
+    if scales.shape != (N, K // GROUP):
+        raise ValueError("shape mismatch in gemv_ternary_x")
+    if out is None:
+        out = torch.empty((b, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    if out.shape != (b, N):
+        raise ValueError("out must be [b, N]")
+    need = gemv_workspace_size(b, K, N)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check("tl_gemv_ternary_x", lib().tl_gemv_ternary_x(
+        _ptr(x), b, K, N, _ptr(signs), _ptr(packed), _ptr(scales), _ptr(out), code, _ptr(workspace),
+        workspace.numel(), _stream(x.device)))
+    return out
+
+
+def quant_act_int8_x(x, signs=None, xq=None, tok_scale=None):
+    """Fused rotation + per-token int8: x bf16 [T,K] -> (xq int8 [T,K], tok_scale f32 [T])
+    (bit-identical to quant_act_int8(hadamard_blk(x, signs)))."""
+    import torch
+    _check_x(x, signs)
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device=x.device) if xq is None else xq
+    tok_scale = torch.empty((T,), dtype=torch.float32, device=x.device) if tok_scale is None else tok_scale
+    _need(xq, "xq", torch.int8, 2)
+    _need(tok_scale, "tok_scale", torch.float32, 1)
+    if xq.shape != (T, K) or tok_scale.shape != (T,):
+        raise ValueError("shape mismatch in quant_act_int8_x")
+    _check("tl_quant_act_int8_x", lib().tl_quant_act_int8_x(_ptr(x), T, K, _ptr(signs), _ptr(xq),
+                                                            _ptr(tok_scale), _stream(x.device)))
+    return xq, tok_scale
 
 
 def gemv_workspace_size(b: int, K: int, N: int) -> int:

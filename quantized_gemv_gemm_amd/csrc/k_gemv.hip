@@ -700,6 +700,12 @@ hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *work
   return hipGetLastError();
 }
 
+hipError_t launch_gemv_prepare_rotated(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
+                                       void *workspace, hipStream_t stream) {
+  const GemvWs w = carve(workspace, b, K);
+  return launch_gemv_prepare_x(x, b, K, signs, w.xhi, w.Kp, w.sigma, stream);
+}
+
 hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t N,
                             const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
                             hipStream_t stream) {

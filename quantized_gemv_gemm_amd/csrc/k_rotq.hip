@@ -1,0 +1,169 @@
+// Fused layer-input kernels: block rotation -> GEMV activation limbs (decode) and
+// block rotation -> per-token int8 quantisation (prefill), so that the rotated
+// activations are never written to memory.
+//
+// Method: qiita.com/nakanokensetsu/items/ecc183fae033565af7cb, "前提" (rotation
+// on the input side), "4. 効いた高速化" (per-token int8 after the rotation).
+// Both kernels produce exactly what the unfused pair produces: the rotation is the
+// same wave routine (exact in binary64, rounded once to f32), the token maximum is
+// over those f32 values, and each element is then converted with the same f32 /
+// binary64 expressions as the GEMV prep and the quantisation kernels.
+//
+// One workgroup per token, W = min(K/1024, 16) waves; wave w rotates blocks
+// w, w + W, ... into registers (at most BPW blocks), the workgroup reduces |x|max,
+// and every lane converts and stores its own elements (lane + 64 j of each block:
+// 64 consecutive bytes per wave store).
+#include "rotate_dev.h"
+
+namespace tl {
+namespace {
+
+constexpr float kLimbRange = 32639.0f;  // as in the GEMV prep: 127 * 257
+constexpr int kMaxWaves = 16;
+
+template <int BPW>
+__device__ __forceinline__ float rotate_token(const uint16_t *__restrict__ xrow,
+                                              const int8_t *__restrict__ signs, int nblk,
+                                              double *lds, int wave, int W, int lane,
+                                              float (&r)[BPW][kRotEPT]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + i * W;
+    if (blk < nblk) {
+      rotate_block_wave(xrow + int64_t(blk) * kHBlock, signs ? signs + int64_t(blk) * kHBlock : nullptr,
+                        lds, lane, r[i]);
+#pragma unroll
+      for (int j = 0; j < kRotEPT; ++j) m = fmaxf(m, fabsf(r[i][j]));
+    }
+  }
+  return m;
+}
+
+// max over the workgroup's W waves; every thread gets it
+__device__ __forceinline__ float token_max(float m, float *red, int wave, int W, int lane) {
+  m = wave_max(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  float v = red[0];
+  for (int w = 1; w < W; ++w) v = fmaxf(v, red[w]);
+  return v;
+}
+
+template <int BPW>
+__global__ __launch_bounds__(64 * kMaxWaves) void gemv_prep_x_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ signs, int64_t K, int64_t Kp, int b,
+    int8_t *__restrict__ xhi, float *__restrict__ sigma) {
+  extern __shared__ double lds[];  // W * kRotLds
+  __shared__ float red[kMaxWaves];
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nblk = int(K / kHBlock);
+  const int64_t t = blockIdx.x;
+  float r[BPW][kRotEPT];
+  const float m = rotate_token<BPW>(x + t * K, signs, nblk, lds + wave * kRotLds, wave, W, lane, r);
+  const float amax = token_max(m, red, wave, W, lane);
+  const float inv = amax > 0.0f ? kLimbRange / amax : 0.0f;
+  if (threadIdx.x == 0) sigma[t] = amax / kLimbRange;
+  int8_t *hrow = xhi + t * Kp;
+  int8_t *lrow = xhi + (int64_t(b) + t) * Kp;
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + i * W;
+    if (blk < nblk) {
+#pragma unroll
+      for (int j = 0; j < kRotEPT; ++j) {
+        int q = (int)rintf(r[i][j] * inv);
+        q = q > 32639 ? 32639 : (q < -32639 ? -32639 : q);
+        const int hi = (q + 128) >> 8;  // floor division: lo lands in [-128, 127]
+        const int64_t e = int64_t(blk) * kHBlock + lane + 64 * j;
+        hrow[e] = (int8_t)hi;
+        lrow[e] = (int8_t)(q - hi * 256);
+      }
+    }
+  }
+}
+
+template <int BPW>
+__global__ __launch_bounds__(64 * kMaxWaves) void quant_x_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ signs, int64_t K,
+    int8_t *__restrict__ xq, float *__restrict__ tok_scale) {
+  extern __shared__ double lds[];  // W * kRotLds
+  __shared__ float red[kMaxWaves];
+  const int W = blockDim.x >> 6, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nblk = int(K / kHBlock);
+  const int64_t t = blockIdx.x;
+  float r[BPW][kRotEPT];
+  const float m = rotate_token<BPW>(x + t * K, signs, nblk, lds + wave * kRotLds, wave, W, lane, r);
+  const float amax = token_max(m, red, wave, W, lane);
+  const float sx = (float)((double)amax / 127.0);
+  if (threadIdx.x == 0) tok_scale[t] = sx;
+  const bool live = sx > 0.0f;
+  const double sxd = (double)sx;
+  int8_t *orow = xq + t * K;
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int blk = wave + i * W;
+    if (blk < nblk) {
+#pragma unroll
+      for (int j = 0; j < kRotEPT; ++j) {
+        int qi = 0;
+        if (live) {
+          qi = (int)rintf((float)((double)r[i][j] / sxd));
+          qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
+        }
+        orow[int64_t(blk) * kHBlock + lane + 64 * j] = (int8_t)qi;
+      }
+    }
+  }
+}
+
+struct FuseShape {
+  int waves, bpw;
+  size_t lds;
+};
+
+FuseShape fuse_shape(int64_t K) {
+  const int nblk = int(K / kHBlock);
+  FuseShape s;
+  s.waves = nblk < kMaxWaves ? nblk : kMaxWaves;
+  s.bpw = (nblk + s.waves - 1) / s.waves;
+  s.lds = size_t(s.waves) * kRotLds * sizeof(double);
+  return s;
+}
+
+}  // namespace
+
+bool fused_input_supported(int64_t K) { return K > 0 && K % kHBlock == 0 && K <= 4 * kMaxWaves * kHBlock; }
+
+hipError_t launch_gemv_prepare_x(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
+                                 int8_t *xhi, int64_t Kp, float *sigma, hipStream_t stream) {
+  const FuseShape s = fuse_shape(K);
+  const dim3 grid{unsigned(b)}, blk{unsigned(64 * s.waves)};
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
+  switch (s.bpw) {
+    case 1: hipLaunchKernelGGL(gemv_prep_x_kernel<1>, grid, blk, s.lds, stream, x, signs, K, Kp, int(b), xhi, sigma); break;
+    case 2: hipLaunchKernelGGL(gemv_prep_x_kernel<2>, grid, blk, s.lds, stream, x, signs, K, Kp, int(b), xhi, sigma); break;
+    case 3: hipLaunchKernelGGL(gemv_prep_x_kernel<3>, grid, blk, s.lds, stream, x, signs, K, Kp, int(b), xhi, sigma); break;
+    default: hipLaunchKernelGGL(gemv_prep_x_kernel<4>, grid, blk, s.lds, stream, x, signs, K, Kp, int(b), xhi, sigma); break;
+  }
+  set_last_kernel("gemv_prep_rotate_limbs");
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, int8_t *xq,
+                          float *tok_scale, hipStream_t stream) {
+  if (T > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const FuseShape s = fuse_shape(K);
+  const dim3 grid{unsigned(T)}, blk{unsigned(64 * s.waves)};
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
+  switch (s.bpw) {
+    case 1: hipLaunchKernelGGL(quant_x_kernel<1>, grid, blk, s.lds, stream, x, signs, K, xq, tok_scale); break;
+    case 2: hipLaunchKernelGGL(quant_x_kernel<2>, grid, blk, s.lds, stream, x, signs, K, xq, tok_scale); break;
+    case 3: hipLaunchKernelGGL(quant_x_kernel<3>, grid, blk, s.lds, stream, x, signs, K, xq, tok_scale); break;
+    default: hipLaunchKernelGGL(quant_x_kernel<4>, grid, blk, s.lds, stream, x, signs, K, xq, tok_scale); break;
+  }
+  set_last_kernel("quant_rotate_int8");
+  return hipGetLastError();
+}
+
+}  // namespace tl

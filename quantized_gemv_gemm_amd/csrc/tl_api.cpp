@@ -176,6 +176,63 @@ int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint
   return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype, st));
 }
 
+int tl_gemv_prepare_x(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (int s = check_gemv_shape(b, K, 0)) return s;
+  if (K % tl::kHBlock) return TL_ERR_SHAPE;
+  if (!tl::fused_input_supported(K)) return TL_ERR_UNSUPPORTED;
+  if (b == 0) return TL_OK;
+  if (!x) return TL_ERR_NULLPTR;
+  const size_t need = tl::gemv_workspace_bytes(b, K, 0);
+  if (!workspace || workspace_bytes < need) return TL_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(workspace) || (signs && !aligned16(signs))) return TL_ERR_ALIGN;
+  Span in[] = {{x, size_t(b) * K * 2}, {signs, signs ? size_t(K) : 0u}};
+  Span out[] = {{workspace, need}};
+  if (any_alias(in, 2, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_gemv_prepare_rotated(x, b, K, signs, workspace,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int tl_gemv_ternary_x(const uint16_t *x, int64_t b, int64_t K, int64_t N, const int8_t *signs,
+                      const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  if (int s = check_gemv_shape(b, K, N)) return s;
+  if (K % tl::kHBlock) return TL_ERR_SHAPE;
+  if (!tl::fused_input_supported(K)) return TL_ERR_UNSUPPORTED;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (b == 0 || N == 0) return TL_OK;
+  if (!x || !packed || !scales || !y) return TL_ERR_NULLPTR;
+  const size_t need = tl::gemv_workspace_bytes(b, K, N);
+  if (!workspace || workspace_bytes < need) return TL_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(y) ||
+      !aligned16(workspace) || (signs && !aligned16(signs)))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(b) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{x, size_t(b) * K * 2}, {signs, signs ? size_t(K) : 0u},
+               {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2}};
+  Span out[] = {{y, ysz}, {workspace, need}};
+  if (any_alias(in, 4, out, 2)) return TL_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = tl::launch_gemv_prepare_rotated(x, b, K, signs, workspace, st);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype, st));
+}
+
+int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, int8_t *xq,
+                        float *tok_scale, void *stream) {
+  if (T < 0 || K <= 0 || K % tl::kHBlock || T >= kMaxDim || K >= kMaxDim) return TL_ERR_SHAPE;
+  if (!tl::fused_input_supported(K)) return TL_ERR_UNSUPPORTED;
+  if (T == 0) return TL_OK;
+  if (!x || !xq || !tok_scale) return TL_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(tok_scale) || (signs && !aligned16(signs)))
+    return TL_ERR_ALIGN;
+  Span in[] = {{x, size_t(T) * K * 2}, {signs, signs ? size_t(K) : 0u}};
+  Span out[] = {{xq, size_t(T) * K}, {tok_scale, size_t(T) * 4}};
+  if (any_alias(in, 2, out, 2)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_quant_x(x, T, K, signs, xq, tok_scale, static_cast<hipStream_t>(stream)));
+}
+
 int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
                       void *stream) {
   if (T < 0 || K <= 0 || K % tl::kGroup || T >= kMaxDim || K >= kMaxDim) return TL_ERR_SHAPE;

@@ -33,6 +33,16 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
                             const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
                             hipStream_t stream);
 
+// fused rotation -> GEMV limbs / int8 quantisation (k_rotq.hip)
+bool fused_input_supported(int64_t K);
+hipError_t launch_gemv_prepare_x(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
+                                 int8_t *xhi, int64_t Kp, float *sigma, hipStream_t stream);
+hipError_t launch_quant_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, int8_t *xq,
+                          float *tok_scale, hipStream_t stream);
+// the GEMV workspace carved for the fused prep (k_gemv.hip)
+hipError_t launch_gemv_prepare_rotated(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
+                                       void *workspace, hipStream_t stream);
+
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
                        const uint32_t *packed, const int8_t *q, const float *row_scale, void *y,

@@ -125,3 +125,27 @@ def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         tl.hadamard_blk(torch.zeros((1, 1024), dtype=torch.bfloat16))
+
+
+def test_fused_input_rejections():
+    L = tl.lib()
+    ws = L.tl_gemv_workspace_size(4, 1024, 256)
+    assert L.tl_gemv_prepare_x(FAKE, 4, 1536, None, FAKE2, ws, None) == 2          # K % 1024
+    assert L.tl_gemv_prepare_x(FAKE, 4, 66560, None, FAKE2, 1 << 30, None) == 6    # K > 65536: unfused calls
+    assert L.tl_gemv_prepare_x(FAKE, 17, 1024, None, FAKE2, ws, None) == 2
+    assert L.tl_gemv_prepare_x(None, 4, 1024, None, FAKE2, ws, None) == 1
+    assert L.tl_gemv_prepare_x(FAKE, 4, 1024, None, FAKE2, ws - 1, None) == 7
+    assert L.tl_gemv_prepare_x(FAKE, 4, 1024, ODD, FAKE2, ws, None) == 3
+    assert L.tl_gemv_prepare_x(FAKE, 4, 1024, None, FAKE, ws, None) == 8
+    assert L.tl_gemv_prepare_x(FAKE, 0, 1024, None, FAKE2, ws, None) == 0
+    gx = lambda b=4, K=1024, N=256, dt=0, w=FAKE5, wb=ws: (FAKE, b, K, N, None, FAKE2, FAKE3, FAKE4, dt, w, wb, None)
+    assert L.tl_gemv_ternary_x(*gx(K=1152)) == 2
+    assert L.tl_gemv_ternary_x(*gx(dt=5)) == 4
+    assert L.tl_gemv_ternary_x(*gx(w=None)) == 7
+    assert L.tl_gemv_ternary_x(*gx(N=0)) == 0
+    assert L.tl_quant_act_int8_x(FAKE, 3, 1152, None, FAKE2, FAKE3, None) == 2
+    assert L.tl_quant_act_int8_x(FAKE, 3, 66560, None, FAKE2, FAKE3, None) == 6
+    assert L.tl_quant_act_int8_x(FAKE, 3, 1024, None, None, FAKE3, None) == 1
+    assert L.tl_quant_act_int8_x(FAKE, 3, 1024, None, FAKE2, ODD, None) == 3
+    assert L.tl_quant_act_int8_x(FAKE, 3, 1024, None, FAKE, FAKE3, None) == 8
+    assert L.tl_quant_act_int8_x(FAKE, 0, 1024, None, FAKE2, FAKE3, None) == 0

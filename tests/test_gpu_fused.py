@@ -1,0 +1,108 @@
+"""Fused layer inputs: rotation -> GEMV limbs and rotation -> int8, checked bit-exactly
+against the unfused sequence (rotation kernel, then prep or quantisation) and
+against the oracle, with and without a sign table."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import REL_TOL, announce, bf16_dev, dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tl():
+    import quantized_gemv_gemm_amd as m
+    m.lib()
+    return m
+
+
+def _signs(K, seed):
+    return np.where(np.random.default_rng(seed).random(K) < 0.5, -1, 1).astype(np.int8)
+
+
+def _limbs(ws, b, K):
+    """hi and lo limb rows [b, K] from a GEMV workspace (rows are K + 16 bytes apart)."""
+    a = ws.cpu().numpy()
+    Kp = K + 16
+    hi = np.stack([a[t * Kp:t * Kp + K] for t in range(b)])
+    lo = np.stack([a[(b + t) * Kp:(b + t) * Kp + K] for t in range(b)])
+    return hi, lo
+
+
+@pytest.mark.parametrize("K,b,signed", [(1024, 1, False), (5120, 4, True), (5120, 16, False),
+                                        (17408, 1, True), (17408, 3, False), (33792, 2, True)])
+def test_gemv_prepare_fused_bitexact(tl, K, b, signed):
+    import torch
+    d = dev()
+    announce(f"gemv_prepare_x K={K} b={b} signed={signed}")
+    xbits = synth.activations(0, 1, 7, b, K)
+    x = bf16_dev(xbits, d)
+    signs = to_dev(_signs(K, K + b), d) if signed else None
+    need = tl.gemv_workspace_size(b, K, 256)
+    w_ref = torch.zeros((need,), dtype=torch.uint8, device=d)
+    w_fus = torch.full((need,), 0x5A, dtype=torch.uint8, device=d)
+    tl.gemv_prepare(tl.hadamard_blk(x, signs), w_ref)
+    tl.gemv_prepare_x(x, w_fus, signs)
+    torch.cuda.synchronize()
+    h0, l0 = _limbs(w_ref, b, K)
+    h1, l1 = _limbs(w_fus, b, K)
+    np.testing.assert_array_equal(h1, h0)
+    np.testing.assert_array_equal(l1, l0)
+    off = (2 * b * (K + 16) + 255) // 256 * 256
+    np.testing.assert_array_equal(w_fus[off:off + 4 * b].cpu().numpy(), w_ref[off:off + 4 * b].cpu().numpy())
+
+
+@pytest.mark.parametrize("K,N,b", [(5120, 1000, 1), (5120, 10240, 8), (17408, 512, 2)])
+def test_gemv_ternary_fused_matches(tl, K, N, b):
+    import torch
+    d = dev()
+    announce(f"gemv_ternary_x K={K} N={N} b={b}")
+    rng = np.random.default_rng(K + N + b)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    packed, _, _ = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    xbits = synth.activations(0, 1, 9, b, K)
+    x = bf16_dev(xbits, d)
+    s_d = to_dev(scales, d)
+    y_ref = tl.gemv_ternary(tl.hadamard_blk(x), packed, s_d, out_dtype=torch.float32)
+    y_fus = tl.gemv_ternary_x(x, packed, s_d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y_fus.cpu().numpy(), y_ref.cpu().numpy())
+    ref = oracle.gemv_ternary(oracle.rotate_exact(synth.bf16_bits_to_f32(xbits)), codes, scales)
+    assert oracle.rel_fro(y_fus.cpu().numpy(), ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("T,K,signed", [(1, 1024, False), (7, 5120, True), (64, 17408, False),
+                                        (33, 17408, True), (300, 5120, False)])
+def test_quant_fused_bitexact(tl, T, K, signed):
+    import torch
+    d = dev()
+    announce(f"quant_act_int8_x T={T} K={K} signed={signed}")
+    xbits = synth.activations(0, 3, 5, T, K)
+    x = bf16_dev(xbits, d)
+    sg = _signs(K, T + K) if signed else None
+    signs = to_dev(sg, d) if signed else None
+    xq0, sx0 = tl.quant_act_int8(tl.hadamard_blk(x, signs))
+    xq1, sx1 = tl.quant_act_int8_x(x, signs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(xq1.cpu().numpy(), xq0.cpu().numpy())
+    np.testing.assert_array_equal(sx1.cpu().numpy(), sx0.cpu().numpy())
+    xq_ref, sx_ref = oracle.quant_act_int8(oracle.rotate_f32(synth.bf16_bits_to_f32(xbits), sg))
+    np.testing.assert_array_equal(xq1.cpu().numpy(), xq_ref)
+    np.testing.assert_array_equal(sx1.cpu().numpy(), sx_ref)
+
+
+def test_quant_fused_zero_token(tl):
+    """A token of zeros: sx = 0 and xq = 0 (no division by zero)."""
+    import torch
+    d = dev()
+    x = torch.zeros((3, 2048), dtype=torch.bfloat16, device=d)
+    x[1, 5] = 1.0
+    xq, sx = tl.quant_act_int8_x(x)
+    torch.cuda.synchronize()
+    assert float(sx[0]) == 0.0 and float(sx[2]) == 0.0 and float(sx[1]) > 0.0
+    assert int(xq[0].abs().sum()) == 0 and int(xq[2].abs().sum()) == 0
