@@ -106,3 +106,34 @@ def test_quant_fused_zero_token(tl):
     torch.cuda.synchronize()
     assert float(sx[0]) == 0.0 and float(sx[2]) == 0.0 and float(sx[1]) > 0.0
     assert int(xq[0].abs().sum()) == 0 and int(xq[2].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("K,N,b,signed", [(5120, 10240, 1, False), (5120, 10240, 2, True),
+                                          (17408, 5120, 1, True), (17408, 5120, 2, False),
+                                          (5120, 34816, 1, False), (5120, 5120, 2, False),
+                                          (1024, 300, 1, True), (3072, 77, 2, False),
+                                          (33792, 1024, 1, False)])
+def test_gemv_ternary_fused_signed_shapes(tl, K, N, b, signed):
+    """Decode at b <= 2 from the raw input, with and without signs, on the layer
+    shapes and ragged ones: bit-identical to the rotation kernel + GEMV sequence
+    and within the relative bound of the oracle."""
+    import torch
+    d = dev()
+    announce(f"gemv_ternary_x signed-shapes K={K} N={N} b={b} signed={signed}")
+    rng = np.random.default_rng(3 * K + N + b)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    packed, _, _ = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    xbits = synth.activations(0, 1, 11, b, K)
+    x = bf16_dev(xbits, d)
+    sg = _signs(K, K + N) if signed else None
+    signs = to_dev(sg, d) if signed else None
+    s_d = to_dev(scales, d)
+    y_ref = tl.gemv_ternary(tl.hadamard_blk(x, signs), packed, s_d, out_dtype=torch.float32)
+    y_fus = torch.full((b, N), float("nan"), dtype=torch.float32, device=d)
+    tl.gemv_ternary_x(x, packed, s_d, signs=signs, out=y_fus)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y_fus.cpu().numpy(), y_ref.cpu().numpy())
+    xr = oracle.rotate_exact(synth.bf16_bits_to_f32(xbits), sg)
+    ref = oracle.gemv_ternary(xr, codes, scales)
+    assert oracle.rel_fro(y_fus.cpu().numpy(), ref) <= REL_TOL
