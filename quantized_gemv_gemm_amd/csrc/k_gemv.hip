@@ -46,11 +46,12 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr float kLimbRange = 32639.0f;  // 127 * 257: hi, lo of 256*hi + lo stay in int8
-constexpr int kRowPad = 16;             // bytes after each limb row: spreads LDS banks
+constexpr int kRowPad = kLimbRowPad;    // bytes after each limb row: spreads LDS banks
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// workspace: hi limbs [b][Kp] then lo limbs [b][Kp] (contiguous), then sigma[16]
+// workspace: the limb region (limb_region_bytes: rows for b <= 8, operand order
+// for b > 8), then sigma[16]
 struct GemvWs {
   int8_t *xhi;
   float *sigma;
@@ -59,7 +60,7 @@ struct GemvWs {
 GemvWs carve(void *workspace, int64_t b, int64_t K) {
   char *ws = static_cast<char *>(workspace);
   const int64_t Kp = K + kRowPad;
-  return {reinterpret_cast<int8_t *>(ws), reinterpret_cast<float *>(ws + align256(2 * size_t(b) * Kp)),
+  return {reinterpret_cast<int8_t *>(ws), reinterpret_cast<float *>(ws + align256(size_t(limb_region_bytes(b, K)))),
           Kp};
 }
 
@@ -105,8 +106,13 @@ __global__ __launch_bounds__(kPrepThreads) void gemv_prep_kernel(const float *__
       hw[c] = h;
       lw[c] = l;
     }
-    *reinterpret_cast<uint4 *>(hrow + i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *reinterpret_cast<uint4 *>(lrow + i) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    if (b > 8) {  // operand order: 16 consecutive k of one token are one lane's 16 bytes
+      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 0)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 1)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      *reinterpret_cast<uint4 *>(hrow + i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4 *>(lrow + i) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
   }
 }
 
@@ -341,17 +347,19 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
   const int tok = LP ? lp_token(col) : token_of_arow(col);
   const int tok_ld = tok < b ? tok : b - 1;
   const int64_t arow = LP ? int64_t(col & 1) * b + tok_ld : tok_ld;
-  const int8_t *gah = limbs + arow * Kp + 32 * qd;      // global limb rows
-  const int8_t *gal = gah + int64_t(b) * Kp;
-  const int8_t *lah = lx + arow * Kp + 32 * qd;         // the same rows in LDS
-  const int8_t *lal = lah + int64_t(b) * Kp;
+  // LP: row-major limb rows; otherwise operand order (1 KB per group, half, limb)
+  const int8_t *gah = LP ? limbs + arow * Kp + 32 * qd : limbs + 16 * lane;  // global limbs
+  const int8_t *gal = LP ? gah + int64_t(b) * Kp : gah + 1024;
+  const int8_t *lah = LP ? lx + arow * Kp + 32 * qd : lx + 16 * lane;        // the same in LDS
+  const int8_t *lal = LP ? lah + int64_t(b) * Kp : lah + 1024;
+  constexpr int kGS = LP ? 128 : 4096, kHS = LP ? 16 : 2048;  // group and half strides
 
   // 1. direct loads into LDS
   stage_scales(scales, N, G, n0, 16 * RB, ls, wave, W, lane);
   if (ALDS) {
     for (int blk = wave; blk * 1024 < lds_limb_bytes; blk += W) {
       const int64_t off = int64_t(blk) * 1024 + 16 * lane;
-      const int64_t src = off < 2 * int64_t(b) * Kp ? off : 0;
+      const int64_t src = off < limb_region_bytes(b, K) ? off : 0;
       __builtin_amdgcn_global_load_lds(limbs + src,
                                        (__attribute__((address_space(3))) void *)(lx + blk * 1024),
                                        16, 0, 0);
@@ -370,8 +378,8 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
         const int64_t gl = min(2 * p + gi, G - 1);  // a padded last group reads a valid row part
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          ga[ALDS ? 0 : pi][gi][h][0] = *reinterpret_cast<const v4i *>(gah + 128 * gl + 16 * h);
-          if (!LP) ga[ALDS ? 0 : pi][gi][h][LP ? 0 : 1] = *reinterpret_cast<const v4i *>(gal + 128 * gl + 16 * h);
+          ga[ALDS ? 0 : pi][gi][h][0] = *reinterpret_cast<const v4i *>(gah + kGS * gl + kHS * h);
+          if (!LP) ga[ALDS ? 0 : pi][gi][h][LP ? 0 : 1] = *reinterpret_cast<const v4i *>(gal + kGS * gl + kHS * h);
         }
       }
     }
@@ -404,8 +412,8 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
       if (ALDS) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          ah[gi][h] = lds_read16(lah + 128 * gl + 16 * h);
-          if (!LP) al[gi][h] = lds_read16(lal + 128 * gl + 16 * h);
+          ah[gi][h] = lds_read16(lah + kGS * gl + kHS * h);
+          if (!LP) al[gi][h] = lds_read16(lal + kGS * gl + kHS * h);
         }
       }
 #pragma unroll
@@ -458,8 +466,9 @@ __device__ __forceinline__ void load_pair(PairSlot<RB> &f, int p, int G, int GP,
     const int gl = min(2 * p + gi, G - 1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f.ah[gi][h] = *reinterpret_cast<const v4i *>(ah + 128 * int64_t(gl) + 16 * h);
-      if (!LP) f.al[gi][h] = *reinterpret_cast<const v4i *>(al + 128 * int64_t(gl) + 16 * h);
+      constexpr int64_t kGS = LP ? 128 : 4096, kHS = LP ? 16 : 2048;  // row-major / operand order
+      f.ah[gi][h] = *reinterpret_cast<const v4i *>(ah + kGS * gl + kHS * h);
+      if (!LP) f.al[gi][h] = *reinterpret_cast<const v4i *>(al + kGS * gl + kHS * h);
     }
   }
 #pragma unroll
@@ -500,8 +509,8 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
 
   const int tok = LP ? lp_token(col) : token_of_arow(col);
   const int tok_ld = tok < b ? tok : b - 1;
-  const int8_t *ah = limbs + int64_t(LP ? (col & 1) * b + tok_ld : tok_ld) * Kp + 32 * qd;
-  const int8_t *al = ah + int64_t(b) * Kp;
+  const int8_t *ah = LP ? limbs + int64_t((col & 1) * b + tok_ld) * Kp + 32 * qd : limbs + 16 * lane;
+  const int8_t *al = LP ? ah + int64_t(b) * Kp : ah + 1024;
   int64_t rbg[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) rbg[rb] = min(int64_t(blockIdx.x) * RB + rb, NB - 1);
@@ -569,7 +578,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   const int64_t G = K / kGroup, GP = (G + 1) / 2;
   const int64_t Kp = K + kRowPad;
   const int nt = b <= 8 ? 2 : int((b + 3) / 4);  // accumulators per row block and lane
-  const int64_t limb_bytes = (2 * b * Kp + 1023) / 1024 * 1024;
+  const int64_t limb_bytes = (limb_region_bytes(b, K) + 1023) / 1024 * 1024;
   GemvPlan p{};
   const bool lp = b <= 8;
   // waves for PMAX pairs each, within the wave cap of the resulting variant
@@ -687,7 +696,7 @@ void launch_ring_r(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
   // two int8 limb planes [b, K + 16] and the per-token scales
-  return align256(2 * size_t(b) * size_t(K + kRowPad)) + align256(16 * sizeof(float));
+  return align256(size_t(limb_region_bytes(b, K))) + align256(16 * sizeof(float));
 }
 
 hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,

@@ -26,6 +26,22 @@ hipError_t launch_hadamard(const uint16_t *x, int64_t T, int64_t K, const int8_t
 hipError_t launch_quant(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
                         hipStream_t stream);
 
+// Decode activation limbs in the GEMV workspace.  b <= 8: row-major rows, hi
+// limbs [b][K + 16] then lo limbs [b][K + 16].  b > 8: the operand order of
+// v_mfma_i32_16x16x64_i8, so that every operand load reads 1 KB contiguously:
+// for group g, 64-k half h and limb l, 64 lanes x 16 bytes, where lane
+// r + 16 q holds A row r (token 4 (r % 4) + r / 4) and k = 128 g + 32 q + 16 h + j.
+constexpr int kLimbRowPad = 16;
+__host__ __device__ inline int64_t limb_region_bytes(int64_t b, int64_t K) {
+  return b > 8 ? 32 * K : 2 * b * (K + kLimbRowPad);
+}
+__host__ __device__ inline int64_t limb_frag_offset(int t, int64_t k, int limb) {
+  const int64_t g = k >> 7;
+  const int kk = int(k & 127);
+  const int row = 4 * (t & 3) + (t >> 2);
+  return ((((g * 2 + ((kk >> 4) & 1)) * 2 + limb) * 64 + row + 16 * (kk >> 5)) << 4) + (kk & 15);
+}
+
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t N);
 hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
                                hipStream_t stream);

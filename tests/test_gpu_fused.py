@@ -24,13 +24,31 @@ def _signs(K, seed):
     return np.where(np.random.default_rng(seed).random(K) < 0.5, -1, 1).astype(np.int8)
 
 
+def _limb_region(b, K):
+    return 32 * K if b > 8 else 2 * b * (K + 16)
+
+
 def _limbs(ws, b, K):
-    """hi and lo limb rows [b, K] from a GEMV workspace (rows are K + 16 bytes apart)."""
+    """hi and lo limb rows [b, K] and the token scales from a GEMV workspace: rows
+    K + 16 bytes apart for b <= 8; for b > 8 the matrix-core operand order (per
+    128-group, 64-k half and limb: 64 lanes x 16 bytes, lane = row + 16 (k%128)//32,
+    row = 4 (t % 4) + t // 4)."""
     a = ws.cpu().numpy()
-    Kp = K + 16
-    hi = np.stack([a[t * Kp:t * Kp + K] for t in range(b)])
-    lo = np.stack([a[(b + t) * Kp:(b + t) * Kp + K] for t in range(b)])
-    return hi, lo
+    if b <= 8:
+        Kp = K + 16
+        hi = np.stack([a[t * Kp:t * Kp + K] for t in range(b)])
+        lo = np.stack([a[(b + t) * Kp:(b + t) * Kp + K] for t in range(b)])
+    else:
+        k = np.arange(K)
+        g, kk = k // 128, k % 128
+        hi, lo = np.empty((b, K), np.uint8), np.empty((b, K), np.uint8)
+        for t in range(b):
+            row = 4 * (t % 4) + t // 4
+            base = (((g * 2 + (kk // 16) % 2) * 2) * 64 + row + 16 * (kk // 32)) * 16 + kk % 16
+            hi[t] = a[base]
+            lo[t] = a[base + 64 * 16]
+    off = (_limb_region(b, K) + 255) // 256 * 256
+    return hi, lo, a[off:off + 4 * b].view(np.float32)
 
 
 @pytest.mark.parametrize("K,b,signed", [(1024, 1, False), (5120, 4, True), (5120, 16, False),
@@ -48,12 +66,17 @@ def test_gemv_prepare_fused_bitexact(tl, K, b, signed):
     tl.gemv_prepare(tl.hadamard_blk(x, signs), w_ref)
     tl.gemv_prepare_x(x, w_fus, signs)
     torch.cuda.synchronize()
-    h0, l0 = _limbs(w_ref, b, K)
-    h1, l1 = _limbs(w_fus, b, K)
+    h0, l0, s0 = _limbs(w_ref, b, K)
+    h1, l1, s1 = _limbs(w_fus, b, K)
     np.testing.assert_array_equal(h1, h0)
     np.testing.assert_array_equal(l1, l0)
-    off = (2 * b * (K + 16) + 255) // 256 * 256
-    np.testing.assert_array_equal(w_fus[off:off + 4 * b].cpu().numpy(), w_ref[off:off + 4 * b].cpu().numpy())
+    np.testing.assert_array_equal(s1, s0)
+    # the limbs are the oracle's fixed-point split of the f32 rotation
+    xr = oracle.rotate_f32(synth.bf16_bits_to_f32(xbits), _signs(K, K + b) if signed else None)
+    amax = np.abs(xr).max(axis=1)
+    np.testing.assert_array_equal(s0, (amax / np.float32(32639.0)).astype(np.float32))
+    v = h0.astype(np.int8).astype(np.int32) * 256 + l0.astype(np.int8).astype(np.int32)
+    assert np.abs(v).max() <= 32639
 
 
 @pytest.mark.parametrize("K,N,b", [(5120, 1000, 1), (5120, 10240, 8), (17408, 512, 2)])
