@@ -599,7 +599,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     // share one copy of the limbs.
     p.kind = 0;
     p.lds_limb_bytes = int(limb_bytes);
-    shape(true, 1, b <= 2 ? 4 : b <= 4 ? 5 : 2);
+    shape(true, 1, b <= 4 ? 5 : 3);
     p.rb = fit_rb(N, size_t(limb_bytes), scale_lds_bytes(16, int(G)) + size_t(p.waves) * nt * 256,
                   p.waves);
     if (b <= 4) p.rb = std::min(p.rb, 2);
