@@ -246,6 +246,54 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[4][2], const float *s
   }
 }
 
+// The same values for a tile that lies inside [M, N], staged through LDS (the
+// activation buffers, free once the K loop is done) so that every lane stores 16
+// contiguous bytes of a row -- a wave writes whole rows -- instead of 2- or
+// 4-byte pieces down a column.  f32 output goes in two passes of 64 rows.
+template <bool kF32>
+__device__ __forceinline__ void epilogue_lds(const v16i (&acc)[4][2], const float *s_tok,
+                                             const float (&rsv)[2], int64_t m0, int64_t n0, int64_t N,
+                                             int wave, int l32, int h, int tid, void *y, int8_t *stage) {
+  constexpr int ES = kF32 ? 4 : 2;         // bytes per output
+  constexpr int PITCH = kBN * ES + 16;     // LDS row pitch (the pad spreads the 4-row steps over banks)
+  constexpr int ROWS = kF32 ? 64 : 128;    // rows per pass
+  constexpr int CPR = kBN * ES / 16;       // 16-byte chunks per row
+  static_assert(ROWS * PITCH <= 3 * kABuf, "staging fits the activation buffers");
+  __syncthreads();  // every wave is done with the activation buffers
+#pragma unroll
+  for (int pass = 0; pass < kBM / ROWS; ++pass) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 64 * wave + 32 * j + l32;
+#pragma unroll
+      for (int mt = pass * (ROWS / 32); mt < (pass + 1) * (ROWS / 32); ++mt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int row = 32 * mt + 8 * rq + 4 * h;
+          const v4f ts = *reinterpret_cast<const v4f *>(s_tok + row);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = ((float)acc[mt][j][4 * rq + i] * rsv[j]) * ts[i];
+            int8_t *dst = stage + (row + i - pass * ROWS) * PITCH + c * ES;
+            if (kF32)
+              *reinterpret_cast<float *>(dst) = v;
+            else
+              *reinterpret_cast<uint16_t *>(dst) = float_to_bf16_bits(v);
+          }
+        }
+    }
+    __syncthreads();
+    char *ybase = static_cast<char *>(y) + ((m0 + pass * ROWS) * N + n0) * ES;
+#pragma unroll
+    for (int k = tid; k < ROWS * CPR; k += kThreads) {
+      const int r = k / CPR, cc = k - r * CPR;
+      *reinterpret_cast<v4u *>(ybase + (int64_t(r) * N) * ES + 16 * cc) =
+          *reinterpret_cast<const v4u *>(stage + r * PITCH + 16 * cc);
+    }
+    if (pass + 1 < kBM / ROWS) __syncthreads();  // the next pass overwrites the staging rows
+  }
+}
+
 inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   Schedule sc;
   sc.mb = int((M + kBM - 1) / kBM);
@@ -412,6 +460,11 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   }
 
   const bool whole = m0 + kBM <= M && n0 + kBN <= N;
+  if (whole && !acc_out && N % 8 == 0) {  // rows of y start on 16-byte boundaries
+    if (y_dtype == TL_F32) epilogue_lds<true>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, y, sA);
+    else epilogue_lds<false>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, y, sA);
+    return;
+  }
   if (y_dtype == TL_F32) {
     if (whole) epilogue<false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
     else epilogue<true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
