@@ -106,6 +106,7 @@ struct Frame {
 };
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
+constexpr int kCoherent = 16;           // cache policy sc1: coherent across the XCDs' L2s
 
 __device__ __forceinline__ void load_a(v4u (&a)[8], const Frame &f, int p) {
 #pragma unroll
@@ -424,15 +425,22 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     // whole-L2 fence is needed: the stores are waited for before the counter is
     // bumped, and the reads are issued after the counter has answered.
     const int slot = g - sc.full;                      // piece index among the left-over tiles
-    int32_t *mine = part + int64_t(slot) * kTileInts;
+    // 16-byte pieces: piece (mt, j, r / 4) of thread tid at ((mt * 2 + j) * 4 + r / 4) * kThreads + tid,
+    // written and read with the system-coherent cache policy (sc1), like the
+    // device-scope atomic accesses, four elements per instruction
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        part + int64_t(slot - piece) * kTileInts, (short)0, int(sc.split * kTileInts * 4), kRsrcWord3);
+    const int mine = piece * kTileInts * 4;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __hip_atomic_store(&mine[((mt * 2 + j) * 16 + r) * kThreads + tid], acc[mt][j][r],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const v4i v = {acc[mt][j][4 * r4], acc[mt][j][4 * r4 + 1], acc[mt][j][4 * r4 + 2], acc[mt][j][4 * r4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128((v4u)v, rp, mine + 16 * (((mt * 2 + j) * 4 + r4) * kThreads + tid), 0,
+                                                 kCoherent);
+        }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every partial store has completed
     __syncthreads();
     if (tid == 0) {
@@ -442,18 +450,19 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     }
     __syncthreads();
     if (!s_last) return;
-    const int first = slot - piece;
     for (int o = 0; o < sc.split; ++o) {
       if (o == piece) continue;
-      int32_t *other = part + int64_t(first + o) * kTileInts;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[mt][j][r] += __hip_atomic_load(&other[((mt * 2 + j) * 16 + r) * kThreads + tid],
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(
+                rp, o * kTileInts * 4 + 16 * (((mt * 2 + j) * 4 + r4) * kThreads + tid), 0, kCoherent);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mt][j][4 * r4 + e] += (int)v[e];
+          }
     }
     if (tid == 0)  // leave the workspace as it was found
       __hip_atomic_store(&counters[tile - sc.full], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
