@@ -232,12 +232,17 @@ def main():
 
     kernel_names = {}
 
-    def step(rec):
-        """One pass of the hot path; appends (kind, key, n_launches, start, end) when rec is a list."""
+    def step(rec, spin=False):
+        """One pass of the hot path; appends (kind, key, n_launches, start, end) when rec is a list.
+        spin: queue a device-side spin before each timed group, so that the group's
+        launches reach the GPU back to back and the events measure device time
+        rather than the pace of the launching Python thread."""
         for b in DECODE_BS:
             tl.gemv_prepare_x(x_dec[b], ws_dec[b])          # rotation fused into the GEMV prep
             if rec is not None:
                 e0, e1 = ev(), ev()
+                if spin:
+                    torch.cuda._sleep(200_000)
                 e0.record(stream)
             for _ in range(DEC_LAYERS):
                 packed, scales, _, _ = qkv[rot["qkv"] % len(qkv)]
@@ -252,6 +257,8 @@ def main():
             tl.quant_act_int8_x(P["x"], xq=P["xq"], tok_scale=P["sx"])   # rotation fused into the quantisation
             if rec is not None:
                 e0, e1 = ev(), ev()
+                if spin:
+                    torch.cuda._sleep(200_000)
                 e0.record(stream)
             for _ in range(PRE_LAYERS):
                 packed, _, q, rs = P["copies"][rot[name] % len(P["copies"])]
@@ -273,15 +280,20 @@ def main():
     gc.collect()
     gc.disable()
     log(f"timing {args.steps} steps")
-    rec = []
     t0, t1 = ev(), ev()
     torch.cuda.synchronize()
     t0.record(stream)
     for _ in range(args.steps):
-        step(rec)
+        step(None)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
+    # per-kernel device times: the same steps again, each timed group queued
+    # behind a spin (the step time above is the plain, spin-free pass)
+    rec = []
+    for _ in range(args.steps):
+        step(rec, spin=True)
+    torch.cuda.synchronize()
 
     gemv_ms = {b: [] for b in DECODE_BS}
     gemm_ms = {"gate_up": [], "down": []}
@@ -289,10 +301,13 @@ def main():
     for kind, key, n, e0, e1 in rec:
         sink[kind][key].append(e0.elapsed_time(e1) / n)
 
-    # the fused input kernels, each timed over a back-to-back run of its own
+    # the fused input kernels: n back-to-back launches between two events, all
+    # queued behind a device-side spin so that the GPU never waits for the host
+    # (small launches issued from Python would otherwise measure the host's pace)
     def run_time(fn, n=20):
         fn()
         e0, e1 = ev(), ev()
+        torch.cuda._sleep(2_000_000)
         e0.record(stream)
         for _ in range(n):
             fn()
