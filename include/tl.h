@@ -167,6 +167,29 @@ int tl_gemv_prepared(const void *workspace, size_t workspace_bytes, int64_t b, i
                      int y_dtype, void *stream);
 
 /*
+ * tl_gemv_ternary_q8 -- decode GEMV against int8 activations (the int8 decode
+ * variant [P1] "5." weighed and set aside for its extra error: the page's dp4a
+ * kernel; here int8 matrix cores).
+ *   [P1] "前提" (y = W (H_blk x)), "4. 効いた高速化" (per-token int8 activations).
+ * in  xq, tok_scale  int8 [b, K], f32 [b]: the rotated activations quantised per
+ *                    token by tl_quant_act_int8 (or tl_quant_act_int8_x)
+ * in  packed, scales as for tl_gemv_ternary
+ * out y       [b, N] of y_dtype:
+ *             y[t,n] = tok_scale[t] * sum_g s[n,g] sum_{k in g} code[n,k] xq[t,k]
+ *             (group sums exact in int32, f32 accumulation over the groups)
+ * One matrix-core chain per group and b*K activation bytes, against two limb
+ * chains and 2*b*K for tl_gemv_ternary; the result carries the activation
+ * rounding (about 8e-3 relative against the exact layer on the generator's data,
+ * against about 3e-5 for tl_gemv_ternary).  No workspace.
+ * Requires 0 <= b <= 16, K > 0, K % 128 == 0, and a wave's share of the group
+ * pairs must fit its registers: every b is supported for K <= 18432, larger K
+ * only while b (K + 16) <= 96 KiB (TL_ERR_UNSUPPORTED otherwise).
+ */
+int tl_gemv_ternary_q8(const int8_t *xq, const float *tok_scale, int64_t b, int64_t K, int64_t N,
+                       const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                       void *stream);
+
+/*
  * tl_quant_act_int8 -- per-token int8 quantisation of rotated activations.
  *   [P1] "4. 効いた高速化" (activations quantised to int8 per token after the
  *   rotation, which evens out outliers).

@@ -32,6 +32,7 @@ from .ternary import (  # noqa: F401
     int8_weight,
     quant_act_int8,
     gemv_ternary,
+    gemv_ternary_q8,
     gemm_int8_acc,
     rescale,
     rel_fro,

@@ -230,6 +230,19 @@ def gemv_ternary(xr: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.nd
     return y
 
 
+def gemv_ternary_q8(xq: np.ndarray, sx: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The decode GEMV on the per-token int8 activations of [P1] §4:
+    y[t, n] = sx[t] * sum_g s[n, g] * sum_{k in g} code[n, k] * xq[t, k]  (binary64).
+
+    [P1] "5." weighs an int8 (dp4a) decode kernel and sets it aside for its extra
+    error; this is that computation, on the same int8 activations the prefill path
+    uses.  It is the decode GEMV of the dequantised activations xq * sx (exact in
+    binary64: an int8 times a float32).
+    """
+    xd = np.asarray(xq, dtype=np.float64) * np.asarray(sx, dtype=np.float64)[:, None]
+    return gemv_ternary(xd, codes, scales)
+
+
 # ---------------------------------------------------------------------------
 # prefill int8 GEMM and rescale  ([P1] §4)
 # ---------------------------------------------------------------------------

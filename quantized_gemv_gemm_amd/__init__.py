@@ -41,6 +41,8 @@ _SIGS = {
     "tl_gemv_prepare": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_sz, _c_p]),
     "tl_gemv_prepared": (ctypes.c_int, [_c_p, _c_sz, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_int,
                                         _c_p]),
+    "tl_gemv_ternary_q8": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_int,
+                                          _c_p]),
     "tl_quant_act_int8": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "tl_gemv_prepare_x": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_sz, _c_p]),
     "tl_gemv_ternary_x": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, ctypes.c_int,
@@ -268,6 +270,29 @@ def gemv_ternary(xr, packed, scales, out_dtype=None, out=None, workspace=None):
     _check("tl_gemv_ternary", lib().tl_gemv_ternary(
         _ptr(xr), b, K, N, _ptr(packed), _ptr(scales), _ptr(out), code, _ptr(workspace),
         workspace.numel(), _stream(xr.device)))
+    return out
+
+
+def gemv_ternary_q8(xq, tok_scale, packed, scales, out_dtype=None, out=None):
+    """Decode GEMV against int8 activations: xq int8 [b,K] and tok_scale f32 [b]
+    (from quant_act_int8 / quant_act_int8_x), packed tiles, scales -> y [b,N]."""
+    import torch
+    _need(xq, "xq", torch.int8, 2)
+    _need(tok_scale, "tok_scale", torch.float32, 1)
+    _need(scales, "scales", torch.float16, 2)
+    b, K = xq.shape
+    N = scales.shape[0]
+    _check_packed(packed, N, K)
+    if scales.shape != (N, K // GROUP) or tok_scale.shape != (b,):
+        raise ValueError("shape mismatch in gemv_ternary_q8")
+    if out is None:
+        out = torch.empty((b, N), dtype=out_dtype or torch.bfloat16, device=xq.device)
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    if out.shape != (b, N):
+        raise ValueError("out must be [b, N]")
+    _check("tl_gemv_ternary_q8", lib().tl_gemv_ternary_q8(
+        _ptr(xq), _ptr(tok_scale), b, K, N, _ptr(packed), _ptr(scales), _ptr(out), code, _stream(xq.device)))
     return out
 
 

@@ -448,6 +448,145 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
 }
 
 // --------------------------------------------------------------------------
+// gemv_q8: the same weight stream against int8 activations (one limb)
+// --------------------------------------------------------------------------
+// y[t, n] = sx_t * sum_g s[n,g] sum_{k in g} code[n,k] xq[t,k] with xq, sx the
+// per-token int8 activations of the prefill path (tl_quant_act_int8).  One MFMA
+// chain per group instead of the two limb chains, and b*K activation bytes
+// instead of 2*b*K; the price is the activation rounding (~8e-3 relative on the
+// generator's data, against ~3e-5 for the two-limb GEMV).  A operand row r holds
+// token 4 (r % 4) + r / 4 (clamped to b - 1), read from the caller's row-major
+// xq: staged in LDS with rows K + 16 bytes apart when b (K + 16) fits, else
+// loaded from L2 into registers with the tiles.
+template <int RB, int NT>
+__device__ __forceinline__ void group_mfma_q8(const v4i (&a)[2], const uint32_t (&w0)[RB],
+                                              const uint32_t (&w1)[RB], const float (&s)[RB],
+                                              float (&acc)[RB][4]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const v4i z = {0, 0, 0, 0};
+    v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], unpack_x64(w0[rb]), z, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[1], unpack_x64(w1[rb]), d, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[rb][i] = fmaf(s[rb], (float)d[i], acc[rb][i]);
+  }
+}
+
+// register budget: ALDS holds RB tiles per pair, otherwise also 4 activation fragments
+// (more than 20 registers' worth of 16-byte loads: 512 threads, 256 VGPRs; the
+// register variant then takes up to 9 pairs per wave, which covers K <= 18432)
+constexpr bool q8_heavy(bool alds, int rb, int pmax) { return alds ? pmax * rb > 10 : pmax * (rb + 4) > 20; }
+constexpr int kQ8PmaxReg = 9;
+
+template <int RB, int NT, int PMAX, bool ALDS>
+__global__ __launch_bounds__(q8_heavy(ALDS, RB, PMAX) ? 512 : 1024) void gemv_q8_kernel(
+    const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int b, int64_t K, int64_t N,
+    const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales, void *__restrict__ y,
+    int y_dtype, int lds_a_bytes) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  int8_t *lx = reinterpret_cast<int8_t *>(smem);
+  char *ls = smem + (ALDS ? lds_a_bytes : 0);
+  const int G = int(K / kGroup);
+  float *red = reinterpret_cast<float *>(ls + scale_lds_bytes(16 * RB, G));
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, qd = lane >> 4;
+  const int GP = (G + 1) >> 1;
+  const int64_t NB = (N + 15) >> 4;
+  const int p_begin = (GP * wave) / W;
+  const int np = (GP * (wave + 1)) / W - p_begin;
+  const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
+  const int64_t Ks = K + kRowPad;  // LDS row pitch
+  const int tok = token_of_arow(col);
+  const int tok_ld = tok < b ? tok : b - 1;
+  const int8_t *ga = xq + int64_t(tok_ld) * K + 32 * qd;
+  const int8_t *la = lx + int64_t(tok_ld) * Ks + 32 * qd;
+
+  // 1. direct loads: the scale block, and (ALDS) the b activation rows, byte P of
+  //    the LDS image holding row P / Ks, column P % Ks (the 16 pad bytes of a row
+  //    load any valid address)
+  stage_scales(scales, N, G, n0, 16 * RB, ls, wave, W, lane);
+  if (ALDS) {
+    for (int c = wave; c * 1024 < lds_a_bytes; c += W) {
+      const int64_t P = int64_t(c) * 1024 + 16 * lane;
+      const int64_t r = P / Ks, off = P - r * Ks;
+      const int8_t *src = r < b && off < K ? xq + r * K + off : xq;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)(lx + c * 1024), 16,
+                                       0, 0);
+    }
+  }
+  asm volatile("" ::: "memory");
+  // 2. register loads of every pair
+  v4i ga_r[ALDS ? 1 : PMAX][2][2];  // [pair][group][64-k half]
+  uint4 wv[PMAX][RB];
+#pragma unroll
+  for (int pi = 0; pi < PMAX; ++pi) {
+    const int p = p_begin + (pi < np ? pi : np - 1);
+    if (!ALDS) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int64_t gl = min(2 * p + gi, G - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ga_r[ALDS ? 0 : pi][gi][h] = *reinterpret_cast<const v4i *>(ga + 128 * gl + 16 * h);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      wv[pi][rb] = load_tile(packed, min(int64_t(blockIdx.x) * RB + rb, NB - 1), GP, p, lane);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<PMAX * (RB + (ALDS ? 0 : 4))>());
+  __builtin_amdgcn_s_barrier();
+
+  // 3. pairs in arrival order
+  float acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[rb][i] = 0.0f;
+#pragma unroll
+  for (int pi = 0; pi < PMAX; ++pi) {
+    const bool live = pi < np;
+    const int p = p_begin + (live ? pi : np - 1);
+    v4i a[2][2], unused[2][2];
+    uint32_t sb[2][RB];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int gl = min(2 * p + gi, G - 1);
+      if (ALDS) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) a[gi][h] = lds_read16(la + 128 * gl + 16 * h);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sb[gi][rb] = lds_read_u16(ls + 2 * ((16 * rb + col) * G + gl));
+    }
+    lds_wait<RB>(a, unused, sb, true);
+    if (!ALDS) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) a[gi][h] = ga_r[ALDS ? 0 : pi][gi][h];
+    }
+    float s0[RB], s1[RB];
+    uint32_t w00[RB], w01[RB], w10[RB], w11[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      s0[rb] = live ? half_bits_to_float(uint16_t(sb[0][rb])) : 0.0f;
+      s1[rb] = live && 2 * p + 1 < G ? half_bits_to_float(uint16_t(sb[1][rb])) : 0.0f;
+      w00[rb] = wv[pi][rb].x;
+      w01[rb] = wv[pi][rb].y;
+      w10[rb] = wv[pi][rb].z;
+      w11[rb] = wv[pi][rb].w;
+    }
+    group_mfma_q8<RB, NT>(a[0], w00, w01, s0, acc);
+    group_mfma_q8<RB, NT>(a[1], w10, w11, s1, acc);
+  }
+  __syncthreads();  // every wave is done with LDS before `red` is written
+  reduce_and_store<RB, NT, false>(acc, red, W, wave, lane, b, n0, N, tok_scale, y, y_dtype);
+}
+
+// --------------------------------------------------------------------------
 // gemv_ring: limb fragments in registers, two pairs of groups in flight per wave
 // (for long K, where a wave's pairs do not all fit in registers at once)
 // --------------------------------------------------------------------------
@@ -692,6 +831,87 @@ void launch_ring_r(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
   }
 }
 
+// int8-activation variant: limbs replaced by the caller's xq rows (see gemv_q8)
+struct Q8Plan {
+  bool ok, alds;
+  int rb, nt, waves, pmax, lds_a;
+  size_t lds;
+  const char *name;
+};
+
+Q8Plan plan_q8(int64_t b, int64_t K, int64_t N) {
+  Q8Plan p{};
+  const int64_t G = K / kGroup, GP = (G + 1) / 2;
+  p.nt = b <= 4 ? 1 : b <= 8 ? 2 : 4;
+  const int64_t lds_a = (b * (K + kRowPad) + 1023) / 1024 * 1024;
+  p.alds = lds_a <= kLdsLimbBudget;
+  p.lds_a = p.alds ? int(lds_a) : 0;
+  p.rb = GP > 40 ? 1 : fit_rb(N, size_t(p.lds_a), scale_lds_bytes(16, int(G)) + 8 * size_t(p.nt) * 256, 8);
+  p.rb = std::min(p.rb, 2);
+  for (int pmax = b <= 4 ? 5 : 3;; ++pmax) {
+    if (pmax > (p.alds ? kPmaxLds : (p.rb == 1 ? kQ8PmaxReg : kPmaxLds))) return p;  // not supported
+    const int cap = q8_heavy(p.alds, p.rb, pmax) ? 8 : kMaxWaves;
+    const int64_t waves = (GP + pmax - 1) / pmax;
+    if (waves <= cap) {
+      p.waves = int(waves);
+      p.pmax = int((GP + waves - 1) / waves);
+      break;
+    }
+  }
+  p.lds = size_t(p.lds_a) + scale_lds_bytes(16 * p.rb, int(G)) +
+          size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * p.nt * 64 * sizeof(float);
+  p.ok = p.lds <= size_t(kLdsPerCU);
+  static const char *names[2][2] = {{"gemv_q8_reg_rb1", "gemv_q8_reg_rb2"}, {"gemv_q8_lds_rb1", "gemv_q8_lds_rb2"}};
+  p.name = names[p.alds ? 1 : 0][p.rb - 1];
+  return p;
+}
+
+struct Q8Args {
+  const int8_t *xq;
+  const float *tok_scale;
+  int64_t b, K, N;
+  const uint32_t *packed;
+  const uint16_t *scales;
+  void *y;
+  int y_dtype;
+  hipStream_t stream;
+};
+
+template <int RB, int NT, int PMAX, bool ALDS>
+void launch_q8_t(const Q8Plan &p, const Q8Args &a) {
+  const dim3 grid(unsigned((a.N + 16 * RB - 1) / (16 * RB)));
+  hipLaunchKernelGGL((gemv_q8_kernel<RB, NT, PMAX, ALDS>), grid, dim3(64 * p.waves), p.lds, a.stream, a.xq,
+                     a.tok_scale, int(a.b), a.K, a.N, a.packed, a.scales, a.y, a.y_dtype, p.lds_a);
+}
+
+template <int RB, int NT, bool ALDS>
+void launch_q8_p(const Q8Plan &p, const Q8Args &a) {
+  switch (p.pmax) {
+    case 1: launch_q8_t<RB, NT, 1, ALDS>(p, a); break;
+    case 2: launch_q8_t<RB, NT, 2, ALDS>(p, a); break;
+    case 3: launch_q8_t<RB, NT, 3, ALDS>(p, a); break;
+    case 4: launch_q8_t<RB, NT, 4, ALDS>(p, a); break;
+    case 5: launch_q8_t<RB, NT, 5, ALDS>(p, a); break;
+    default:
+      if constexpr (!ALDS && RB == 1) {  // long K: the register variant with up to 9 pairs
+        switch (p.pmax) {
+          case 6: launch_q8_t<RB, NT, 6, ALDS>(p, a); break;
+          case 7: launch_q8_t<RB, NT, 7, ALDS>(p, a); break;
+          case 8: launch_q8_t<RB, NT, 8, ALDS>(p, a); break;
+          default: launch_q8_t<RB, NT, 9, ALDS>(p, a); break;
+        }
+      }
+      break;
+  }
+}
+
+template <int RB, bool ALDS>
+void launch_q8_n(const Q8Plan &p, const Q8Args &a) {
+  if (p.nt == 1) launch_q8_p<RB, 1, ALDS>(p, a);
+  else if (p.nt == 2) launch_q8_p<RB, 2, ALDS>(p, a);
+  else launch_q8_p<RB, 4, ALDS>(p, a);
+}
+
 }  // namespace
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
@@ -727,6 +947,24 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
   else if (p.kind == 1) launch_stream<false>(p, grid, a);
   else if (p.rb == 2) launch_ring_r<2>(p, grid, a);
   else launch_ring_r<1>(p, grid, a);
+  set_last_kernel(p.name);
+  return hipGetLastError();
+}
+
+bool gemv_q8_supported(int64_t b, int64_t K, int64_t N) { return plan_q8(b, K, N).ok; }
+
+hipError_t launch_gemv_q8(const int8_t *xq, const float *tok_scale, int64_t b, int64_t K, int64_t N,
+                          const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                          hipStream_t stream) {
+  const Q8Plan p = plan_q8(b, K, N);
+  if (!p.ok) return hipErrorInvalidValue;
+  const Q8Args a{xq, tok_scale, b, K, N, packed, scales, y, y_dtype, stream};
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
+  if (p.alds) {
+    if (p.rb == 2) launch_q8_n<2, true>(p, a); else launch_q8_n<1, true>(p, a);
+  } else {
+    if (p.rb == 2) launch_q8_n<2, false>(p, a); else launch_q8_n<1, false>(p, a);
+  }
   set_last_kernel(p.name);
   return hipGetLastError();
 }

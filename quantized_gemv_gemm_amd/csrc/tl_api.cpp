@@ -233,6 +233,25 @@ int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *s
   return from_hip(tl::launch_quant_x(x, T, K, signs, xq, tok_scale, static_cast<hipStream_t>(stream)));
 }
 
+int tl_gemv_ternary_q8(const int8_t *xq, const float *tok_scale, int64_t b, int64_t K, int64_t N,
+                       const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                       void *stream) {
+  if (int s = check_gemv_shape(b, K, N)) return s;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (b == 0 || N == 0) return TL_OK;
+  if (!xq || !tok_scale || !packed || !scales || !y) return TL_ERR_NULLPTR;
+  if (!aligned16(xq) || !aligned16(packed) || !aligned16(scales) || !aligned16(y)) return TL_ERR_ALIGN;
+  if (!tl::gemv_q8_supported(b, K, N)) return TL_ERR_UNSUPPORTED;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(b) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{xq, size_t(b) * K}, {tok_scale, size_t(b) * 4}, {packed, size_t(tl::packed_words(N, K)) * 4},
+               {scales, size_t(N) * G * 2}};
+  Span out[] = {{y, ysz}};
+  if (any_alias(in, 4, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_gemv_q8(xq, tok_scale, b, K, N, packed, scales, y, y_dtype,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *tok_scale,
                       void *stream) {
   if (T < 0 || K <= 0 || K % tl::kGroup || T >= kMaxDim || K >= kMaxDim) return TL_ERR_SHAPE;

@@ -91,6 +91,21 @@ def test_gemv_rejections():
     assert L.tl_gemv_ternary(*args(N=0)) == 0
 
 
+def test_gemv_q8_rejections():
+    L = tl.lib()
+    args = lambda b=4, K=1024, N=256, sx=FAKE5, y=FAKE4, dt=0: (FAKE, sx, b, K, N, FAKE2, FAKE3, y, dt, None)
+    assert L.tl_gemv_ternary_q8(*args(b=17)) == 2
+    assert L.tl_gemv_ternary_q8(*args(K=1000)) == 2
+    assert L.tl_gemv_ternary_q8(*args(dt=7)) == 4
+    assert L.tl_gemv_ternary_q8(*args(y=None)) == 1
+    assert L.tl_gemv_ternary_q8(*args(sx=None)) == 1
+    assert L.tl_gemv_ternary_q8(*args(y=ODD)) == 3
+    assert L.tl_gemv_ternary_q8(*args(y=FAKE)) == 8
+    assert L.tl_gemv_ternary_q8(*args(b=16, K=128 * 200)) == 6   # too many group pairs per wave
+    assert L.tl_gemv_ternary_q8(*args(b=0)) == 0
+    assert L.tl_gemv_ternary_q8(*args(N=0)) == 0
+
+
 def test_quant_rejections():
     L = tl.lib()
     assert L.tl_quant_act_int8(FAKE, 3, 100, FAKE2, FAKE3, None) == 2

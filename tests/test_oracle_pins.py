@@ -350,6 +350,46 @@ def test_gemv_pins():
     check_gemv(oracle.gemv_ternary)
 
 
+def check_gemv_q8(gemv_q8):
+    """int8-activation decode: brute force with integer group sums, a closed form,
+    and the scale of each token."""
+    rng = np.random.default_rng(21)
+    b, K, N = 3, 384, 5
+    xq = rng.integers(-127, 128, (b, K)).astype(np.int8)
+    sx = rng.random(b).astype(np.float32) + np.float32(0.5)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    sc = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    y = gemv_q8(xq, sx, codes, sc)
+    ref = np.zeros((b, N))
+    for t in range(b):
+        for n in range(N):
+            acc = 0.0
+            for g in range(K // 128):
+                isum = sum(int(codes[n, k]) * int(xq[t, k]) for k in range(128 * g, 128 * g + 128))
+                acc += float(sc[n, g]) * isum
+            ref[t, n] = float(sx[t]) * acc
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+    # closed form: a single activation 1 at m with sx = 1 picks code[n, m] * s[n, m//128]
+    for m in (0, 129, 383):
+        e = np.zeros((1, K), dtype=np.int8)
+        e[0, m] = 1
+        np.testing.assert_array_equal(gemv_q8(e, np.ones(1, np.float32), codes, sc)[0],
+                                      codes[:, m].astype(np.float64) * sc[:, m // 128].astype(np.float64))
+
+
+def test_gemv_q8_pins():
+    check_gemv_q8(oracle.gemv_ternary_q8)
+    # against the exact layer it differs by the activation rounding
+    # only: with xq from the oracle's own quantisation the error is that of [P1] §4
+    rng = np.random.default_rng(22)
+    xr = rng.standard_normal((4, 1024))
+    codes = rng.integers(-1, 2, (64, 1024)).astype(np.int8)
+    sc = np.exp(-4 + 0.5 * rng.standard_normal((64, 8))).astype(np.float16)
+    xq, sx = oracle.quant_act_int8(xr.astype(np.float32))
+    e = oracle.rel_fro(oracle.gemv_ternary_q8(xq, sx, codes, sc), oracle.gemv_ternary(xr, codes, sc))
+    assert 1e-3 < e < 2e-2, e
+
+
 # ---------------------------------------------------------------------------
 # int8 GEMM and rescale
 # ---------------------------------------------------------------------------
@@ -466,6 +506,10 @@ def _gemv_wrong_group(xr, codes, scales):         # scale index off by one group
     return oracle.gemv_ternary(xr, codes, np.roll(np.asarray(scales), 1, axis=1))
 
 
+def _gemv_q8_no_token_scale(xq, sx, codes, scales):  # the per-token scale left out
+    return oracle.gemv_ternary(np.asarray(xq, dtype=np.float64), codes, scales)
+
+
 def _gemm_transposed_q(xq, codes, q):             # q indexed by k % G instead of k // 128
     G = q.shape[1]
     W = np.asarray(codes, dtype=np.int64) * np.asarray(q, dtype=np.int64)[:, np.arange(codes.shape[1]) % G]
@@ -481,6 +525,7 @@ def _gemm_transposed_q(xq, codes, q):             # q indexed by k % G instead o
     (lambda: check_scales(_decomp_half_up), "scale-ties"),
     (lambda: check_quant(_quant_mul_recip), "quant-formula"),
     (lambda: check_gemv(_gemv_wrong_group), "gemv-group"),
+    (lambda: check_gemv_q8(_gemv_q8_no_token_scale), "gemv-q8-token-scale"),
     (lambda: check_gemm(_gemm_transposed_q), "gemm-q-index"),
 ])
 def test_planted_mistakes_are_caught(mutant, check):
