@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-stack", action="store_true", help="skip the 64-block whole-stack pass")
     p.add_argument("--stack-steps", type=int, default=5)
+    p.add_argument("--bsweep", action="store_true",
+                   help="token-count sweep of the two layer paths (GEMV vs int8 GEMM) instead of the bench")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -185,6 +187,10 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.bsweep:
+        bsweep(tl, torch, dev, log)
+        return
 
     # ---------------- weights (packed once, cloned into rotating copies) ----------------
     def make_layer(config, li, K, N):
@@ -402,6 +408,106 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+SWEEP_BS = (1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48, 64, 96, 128, 192, 256, 384, 512)
+SWEEP_SHAPES = (("qkv", 1, 0, 5120, 10240), ("gate_up", 2, 0, 5120, 34816), ("down", 2, 1, 17408, 5120))
+
+
+def bsweep(tl, torch, dev, log, n=20):
+    """Whole-layer time from the raw bf16 input, per token count T, for the two paths:
+    'gemv' = rotation fused into the limb prep, then the two-limb GEMV (T <= 64);
+    'int8' = rotation fused into the per-token int8 quantisation, then the int8 GEMM
+    + rescale.  Each point: n back-to-back layers over rotating weight copies,
+    queued behind a device-side spin, between two HIP events on the launch stream.
+    Prints one JSON line per (shape, T) and one per shape with the crossover."""
+    import gc
+
+    import synth
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    bf16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    # the spin must outlast the host's issue of n layers (two binding calls each)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    torch.cuda._sleep(1_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spin_ms_per_m = e0.elapsed_time(e1)
+    spin = int(1_000_000 * (n * 0.2) / spin_ms_per_m)      # about 200 us of device spin per layer
+    print(json.dumps({"spin_cycles": spin, "spin_ms": round(spin * spin_ms_per_m / 1e6, 2)}), flush=True)
+    for name, config, li, K, N in SWEEP_SHAPES:
+        L = synth.LayerInputs(0, config, li, K, N)
+        codes = L.codes_torch(dev)
+        scales = torch.from_numpy(L.scales()).to(dev)
+        packed, q, rs = tl.pack_weights(codes, scales)
+        del codes
+        per = packed.numel() * 4 + scales.numel() * 2 + q.numel() + rs.numel() * 4
+        R = max(2, math.ceil(ROTATE_BYTES / per))
+        copies = [(packed, scales, q, rs)] + [(packed.clone(), scales.clone(), q.clone(), rs.clone())
+                                              for _ in range(R - 1)]
+        x_all = bf16(synth.activations(0, config, 100 + li, max(SWEEP_BS), K))
+        rows = []
+        for T in SWEEP_BS:
+            x = x_all[:T]
+            y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+            sx = torch.empty((T,), dtype=torch.float32, device=dev)
+            ws = (torch.empty((tl.gemv_workspace_size(T, K, N),), dtype=torch.uint8, device=dev)
+                  if T <= 64 else None)
+            rot = [0]
+
+            def nxt():
+                c = copies[rot[0] % len(copies)]
+                rot[0] += 1
+                return c
+
+            def gemv():
+                pk, sc, _, _ = nxt()
+                tl.gemv_ternary_x(x, pk, sc, out=y, workspace=ws)
+
+            def int8():
+                pk, _, qq, r = nxt()
+                tl.quant_act_int8_x(x, xq=xq, tok_scale=sx)
+                tl.gemm_int8_rescale(xq, sx, pk, qq, r, out=y)
+
+            lws = torch.zeros((tl.linear_workspace_size(T, K, N),), dtype=torch.uint8, device=dev)
+
+            def linear():
+                pk, sc, qq, r = nxt()
+                tl.linear_apply(x, pk, sc, qq, r, out=y, workspace=lws)
+
+            row = {"shape": name, "K": K, "N": N, "T": T,
+                   "path": "gemv" if tl.linear_path(T, K, N) == tl.PATH_GEMV else "int8"}
+            for pname, fn in (("gemv", gemv), ("int8", int8), ("linear", linear)):
+                if pname == "gemv" and ws is None:
+                    continue
+                fn()
+                torch.cuda.synchronize()
+                gc.disable()
+                e0, e1 = ev(), ev()
+                torch.cuda._sleep(spin)
+                e0.record(stream)
+                h0 = time.perf_counter()
+                for _ in range(n):
+                    fn()
+                host_us = (time.perf_counter() - h0) / n * 1e6
+                e1.record(stream)
+                torch.cuda.synchronize()
+                gc.enable()
+                row[pname + "_us"] = round(e0.elapsed_time(e1) / n * 1e3, 2)
+                row[pname + "_host_us"] = round(host_us, 1)   # issue pace; the spin covers it
+            row["faster"] = "gemv" if row.get("gemv_us", 1e30) <= row["int8_us"] else "int8"
+            del lws
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+        gemv_wins = [r["T"] for r in rows if r["faster"] == "gemv"]
+        print(json.dumps({"shape": name, "K": K, "N": N,
+                          "gemv_faster_up_to": max(gemv_wins) if gemv_wins else 0,
+                          "gemv_faster_at": gemv_wins}), flush=True)
+        log(f"bsweep {name} done")
+        del copies, packed, scales, q, rs
+        torch.cuda.empty_cache()
 
 
 def stack_pass(tl, torch, dev, steps, log):

@@ -8,7 +8,7 @@
  *     128-element group along K ([P1] "前提");
  *   - the input is rotated by a block-wise Sylvester Hadamard transform with
  *     1024-wide blocks and an optional sign table ([P1] "前提", "1. TP=2 への移植");
- *   - decode computes y = W (H_blk x) for 1..16 tokens;
+ *   - decode computes y = W (H_blk x) for 1..64 tokens;
  *   - prefill decomposes each scale as q = round(127 s / smax) so that
  *     code * q is exact in int8, quantises the rotated activations to int8 per
  *     token, and runs one int8 x int8 -> int32 GEMM followed by a per-row and
@@ -129,7 +129,7 @@ int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs
                     void *stream);
 
 /*
- * tl_gemv_ternary -- decode GEMV, y = W xr for 1..16 tokens.
+ * tl_gemv_ternary -- decode GEMV, y = W xr for 1..64 tokens.
  *   [P1] "前提" (y = W (H_blk x), W = code * group scale).
  * in  xr      f32    [b, K]      rotated activations (tl_hadamard_blk output)
  * in  packed  uint32 tiles      from tl_pack_weights (tl_packed_bytes(N, K) bytes)
@@ -142,7 +142,11 @@ int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs
  * split into two int8 limbs (scale amax_t / 32639), and group results are
  * accumulated in f32.  Relative Frobenius error against exact arithmetic is
  * about 3e-5 on the generator's data (bound used by the tests: 1e-3).
- * Requires 0 <= b <= 16, K > 0, K % 128 == 0.
+ * One matrix-core operand holds 16 tokens: b > 16 runs ceil(b/16) chunks of 16
+ * tokens side by side in the same launch, each streaming the weights itself
+ * (chunks of one row range share an L2), so the time grows with the chunk count
+ * (tl_linear_path tells when the prefill path is the faster choice).
+ * Requires 0 <= b <= 64, K > 0, K % 128 == 0.
  */
 size_t tl_gemv_workspace_size(int64_t b, int64_t K, int64_t N);
 int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint32_t *packed,
@@ -252,6 +256,42 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
                          int64_t N, const uint32_t *packed, const int8_t *q,
                          const float *row_scale, void *y, int y_dtype, int32_t *acc_out,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * tl_linear_apply -- the whole layer from the raw input, y = W (H_blk x) for T
+ * tokens, on the path that tl_linear_path(T, K, N) names:
+ *   TL_PATH_GEMV  rotation fused into the limb prep, then the two-limb GEMV
+ *                 (tl_gemv_ternary_x); relative error about 3e-5;
+ *   TL_PATH_INT8  rotation fused into the per-token int8 quantisation, then the
+ *                 int8 GEMM + rescale (tl_quant_act_int8_x, tl_gemm_int8_rescale);
+ *                 relative error about 1e-2 against the exact layer (the
+ *                 activation and scale rounding of [P1] "4. 効いた高速化").
+ *   [P1] "前提" (the layer), "4. 効いた高速化" (the prefill path); the choice by
+ *   token count mirrors the page's decode / prefill split.
+ * tl_linear_path: up to 16 tokens the GEMV; 17..64 tokens the GEMV while
+ * ceil(T/16) * ceil(N/64) <= 640 (its chunk workgroups fit in about 2.5 rounds of
+ * the 256 compute units), else the int8 path; above 64 tokens the int8 path.
+ * The rule follows a measured token sweep of both paths at the qkv
+ * (5120 -> 10240), gate_up (5120 -> 34816) and down (17408 -> 5120) shapes.
+ * in  x          bf16 [T, K] raw layer input; signs as in tl_hadamard_blk
+ * in  packed, scales, q, row_scale  from tl_pack_weights (all four are required
+ *                whichever path runs)
+ * out y          [T, N] of y_dtype
+ * workspace      device scratch of at least tl_linear_workspace_size(T, K, N)
+ *                bytes, zero-filled before its first use (its first KiB holds the
+ *                int8 GEMM's split-K counters, which every call leaves at zero, as
+ *                for tl_gemm_int8_rescale); calls that overlap in time must not
+ *                share one.
+ * Requires K % 1024 == 0 and K <= 65536 (TL_ERR_UNSUPPORTED above).
+ */
+#define TL_PATH_GEMV 0
+#define TL_PATH_INT8 1
+int tl_linear_path(int64_t T, int64_t K, int64_t N);
+size_t tl_linear_workspace_size(int64_t T, int64_t K, int64_t N);
+int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const int8_t *signs,
+                    const uint32_t *packed, const uint16_t *scales, const int8_t *q,
+                    const float *row_scale, void *y, int y_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

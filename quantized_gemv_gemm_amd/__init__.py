@@ -51,7 +51,13 @@ _SIGS = {
     "tl_gemm_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "tl_gemm_int8_rescale": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
                                             ctypes.c_int, _c_p, _c_p, _c_sz, _c_p]),
+    "tl_linear_path": (ctypes.c_int, [_c_i64, _c_i64, _c_i64]),
+    "tl_linear_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
+    "tl_linear_apply": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                       ctypes.c_int, _c_p, _c_sz, _c_p]),
 }
+
+PATH_GEMV, PATH_INT8 = 0, 1
 
 
 def lib():
@@ -248,7 +254,7 @@ def gemv_workspace_size(b: int, K: int, N: int) -> int:
 
 
 def gemv_ternary(xr, packed, scales, out_dtype=None, out=None, workspace=None):
-    """xr f32 [b,K] (b <= 16), packed tiles, scales fp16 [N,K/128] -> y [b,N]."""
+    """xr f32 [b,K] (b <= 64), packed tiles, scales fp16 [N,K/128] -> y [b,N]."""
     import torch
     _need(xr, "xr", torch.float32, 2)
     _need(scales, "scales", torch.float16, 2)
@@ -395,3 +401,56 @@ def gemm_int8_rescale(xq, tok_scale, packed, q, row_scale, out_dtype=None, out=N
         _ptr(xq), _ptr(tok_scale), M, K, N, _ptr(packed), _ptr(q), _ptr(row_scale), _ptr(out), code,
         _ptr(acc_out), _ptr(workspace), ws_bytes, _stream(xq.device)))
     return (out, acc_out) if acc_out is not None else out
+
+
+def linear_path(T: int, K: int, N: int) -> int:
+    """PATH_GEMV or PATH_INT8: the path linear_apply takes for T tokens of a K -> N layer."""
+    return int(lib().tl_linear_path(T, K, N))
+
+
+def linear_workspace_size(T: int, K: int, N: int) -> int:
+    return int(lib().tl_linear_workspace_size(T, K, N))
+
+
+_LIN_WS = {}
+
+
+def _linear_workspace(device, nbytes):
+    """A zero-filled layer workspace per (device, stream), grown on demand (every
+    call leaves its counter region at zero, so one buffer serves every call)."""
+    import torch
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _LIN_WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros((nbytes,), dtype=torch.uint8, device=device)
+        _LIN_WS[key] = ws
+    return ws
+
+
+def linear_apply(x, packed, scales, q, row_scale, signs=None, out_dtype=None, out=None, workspace=None):
+    """The whole layer from the raw input: x bf16 [T,K] -> y [T,N], on the path
+    linear_path(T, K, N) names (two-limb GEMV, or int8 quantisation + int8 GEMM)."""
+    import torch
+    _check_x(x, signs)
+    _need(scales, "scales", torch.float16, 2)
+    _need(q, "q", torch.int8, 2)
+    _need(row_scale, "row_scale", torch.float32, 1)
+    T, K = x.shape
+    N = scales.shape[0]
+    _check_packed(packed, N, K)
+    if scales.shape != (N, K // GROUP) or q.shape != (N, K // GROUP) or row_scale.shape != (N,):
+        raise ValueError("shape mismatch in linear_apply")
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    if out.shape != (T, N):
+        raise ValueError("out must be [T, N]")
+    need = linear_workspace_size(T, K, N)
+    if workspace is None:
+        workspace = _linear_workspace(x.device, max(need, 1))
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check("tl_linear_apply", lib().tl_linear_apply(
+        _ptr(x), T, K, N, _ptr(signs), _ptr(packed), _ptr(scales), _ptr(q), _ptr(row_scale), _ptr(out), code,
+        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out

@@ -51,7 +51,7 @@ constexpr int kRowPad = kLimbRowPad;    // bytes after each limb row: spreads LD
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // workspace: the limb region (limb_region_bytes: rows for b <= 8, operand order
-// for b > 8), then sigma[16]
+// for b > 8), then sigma[b]
 struct GemvWs {
   int8_t *xhi;
   float *sigma;
@@ -107,8 +107,8 @@ __global__ __launch_bounds__(kPrepThreads) void gemv_prep_kernel(const float *__
       lw[c] = l;
     }
     if (b > 8) {  // operand order: 16 consecutive k of one token are one lane's 16 bytes
-      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 0)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 1)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 0, K)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 1, K)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     } else {
       *reinterpret_cast<uint4 *>(hrow + i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *reinterpret_cast<uint4 *>(lrow + i) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -139,6 +139,20 @@ __device__ __forceinline__ int token_of_arow(int r) { return 4 * (r & 3) + (r >>
 // in one lane -- D rows 4q, 4q+1 are hi, lo of token 2q and 4q+2, 4q+3 those of
 // token 2q+1 -- which halves the MFMAs and activation reads of the two-limb form.
 __device__ __forceinline__ int lp_token(int r) { return 2 * (r >> 2) + ((r >> 1) & 1); }
+
+// More than 16 tokens: grid row blockIdx.y takes token chunk c = 16 c .. 16 c + 15
+// (operand-order limbs at 32 K c, sigma and y rows from 16 c); b becomes the
+// chunk's token count.
+template <class PL, class PS, class PY>  // the kernels' (restrict-qualified) parameter types
+__device__ __forceinline__ void select_chunk(PL &limbs, PS &sigma, PY &y, int &b, int64_t K, int64_t N,
+                                             int y_dtype) {
+  const int c = blockIdx.y;
+  if (c == 0) return;
+  limbs += 32 * K * c;
+  sigma += kTokChunk * c;
+  y = static_cast<char *>(y) + int64_t(kTokChunk) * c * N * (y_dtype == TL_F32 ? 4 : 2);
+  b = min(kTokChunk, b - kTokChunk * c);
+}
 
 // one group for RB row blocks: two 64-k halves x two limbs, then f32 accumulation.
 // w0/w1 are the lane's packed words for the group's two 64-k halves.
@@ -329,6 +343,8 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
     void *__restrict__ y, int y_dtype, int lds_limb_bytes) {
   constexpr int NA = LP ? 4 : 8;  // A fragment loads per pair when not ALDS
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  select_chunk(limbs, sigma, y, b, K, N, y_dtype);
+  const int64_t region = LP ? limb_region_bytes(b, K) : 32 * K;  // this chunk's limbs
   int8_t *lx = reinterpret_cast<int8_t *>(smem);
   char *ls = smem + (ALDS ? lds_limb_bytes : 0);
   const int G = int(K / kGroup);
@@ -359,7 +375,7 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
   if (ALDS) {
     for (int blk = wave; blk * 1024 < lds_limb_bytes; blk += W) {
       const int64_t off = int64_t(blk) * 1024 + 16 * lane;
-      const int64_t src = off < limb_region_bytes(b, K) ? off : 0;
+      const int64_t src = off < region ? off : 0;
       __builtin_amdgcn_global_load_lds(limbs + src,
                                        (__attribute__((address_space(3))) void *)(lx + blk * 1024),
                                        16, 0, 0);
@@ -633,6 +649,7 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
     int64_t Kp, int64_t N, const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
     void *__restrict__ y, int y_dtype) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  select_chunk(limbs, sigma, y, b, K, N, y_dtype);
   char *ls = smem;  // scale block of the workgroup's rows, then (W - 1) * RB * NT * 64 floats
   float *red = reinterpret_cast<float *>(smem + scale_lds_bytes(16 * RB, int(K / kGroup)));
   const int W = blockDim.x >> 6;
@@ -687,6 +704,7 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
 struct GemvPlan {
   int kind;  // 0: stream with limbs in LDS, 1: stream with limbs from L2, 2: ring
   int rb, waves, pmax;
+  int chunks;  // grid rows: token chunks of 16
   int lds_limb_bytes;
   size_t lds_bytes;
   const char *name;
@@ -704,18 +722,20 @@ constexpr int kCUs = 256;
 constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kWavesPerCU = 32;
 
-int fit_rb(int64_t N, size_t lds_fixed, size_t lds_per_rb, int waves) {
+int fit_rb(int64_t N, int64_t chunks, size_t lds_fixed, size_t lds_per_rb, int waves) {
   for (int rb = 1; rb <= 4; rb *= 2) {
     const size_t lds = lds_fixed + lds_per_rb * rb;
     const int64_t per_cu = std::min<int64_t>(int64_t(kLdsPerCU / lds), kWavesPerCU / waves);
-    if ((N + 16 * rb - 1) / (16 * rb) <= per_cu * kCUs) return rb;
+    if ((N + 16 * rb - 1) / (16 * rb) * chunks <= per_cu * kCUs) return rb;
   }
   return 4;
 }
 
 GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
+  // more than 16 tokens: one grid row per chunk of 16, each shaped like b = 16
+  const int64_t chunks = b > kTokChunk ? limb_chunks(b) : 1;
+  b = std::min<int64_t>(b, kTokChunk);
   const int64_t G = K / kGroup, GP = (G + 1) / 2;
-  const int64_t Kp = K + kRowPad;
   const int nt = b <= 8 ? 2 : int((b + 3) / 4);  // accumulators per row block and lane
   const int64_t limb_bytes = (limb_region_bytes(b, K) + 1023) / 1024 * 1024;
   GemvPlan p{};
@@ -739,7 +759,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     p.kind = 0;
     p.lds_limb_bytes = int(limb_bytes);
     shape(true, 1, b <= 4 ? 5 : 3);
-    p.rb = fit_rb(N, size_t(limb_bytes), scale_lds_bytes(16, int(G)) + size_t(p.waves) * nt * 256,
+    p.rb = fit_rb(N, chunks, size_t(limb_bytes), scale_lds_bytes(16, int(G)) + size_t(p.waves) * nt * 256,
                   p.waves);
     if (b <= 4) p.rb = std::min(p.rb, 2);
     shape(true, p.rb, p.pmax);
@@ -763,6 +783,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
                                     {"gemv_stream_reg_rb1", "gemv_stream_reg_rb2", "gemv_stream_reg_rb4"},
                                     {"gemv_ring_rb1", "gemv_ring_rb2", "gemv_ring_rb2"}};
   p.name = names[p.kind][p.rb == 4 ? 2 : p.rb - 1];
+  p.chunks = int(chunks);
   return p;
 }
 
@@ -804,7 +825,7 @@ void launch_stream_p(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
 
 template <int RB, bool ALDS>
 void launch_stream_n(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
-  switch ((a.b + 3) / 4) {
+  switch ((std::min<int64_t>(a.b, kTokChunk) + 3) / 4) {
     case 1:
     case 2: launch_stream_p<RB, 2, true, ALDS>(p, grid, a); break;
     case 3: launch_stream_p<RB, 3, false, ALDS>(p, grid, a); break;
@@ -823,7 +844,7 @@ template <int RB>
 void launch_ring_r(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
   const dim3 blk(64 * p.waves);
   const GemvWs &w = *a.w;
-  switch ((a.b + 3) / 4) {
+  switch ((std::min<int64_t>(a.b, kTokChunk) + 3) / 4) {
     case 1:
     case 2: hipLaunchKernelGGL((gemv_ring_kernel<RB, 2, true>), grid, blk, p.lds_bytes, a.stream, w.xhi, w.sigma, int(a.b), a.K, w.Kp, a.N, a.packed, a.scales, a.y, a.y_dtype); break;
     case 3: hipLaunchKernelGGL((gemv_ring_kernel<RB, 3, false>), grid, blk, p.lds_bytes, a.stream, w.xhi, w.sigma, int(a.b), a.K, w.Kp, a.N, a.packed, a.scales, a.y, a.y_dtype); break;
@@ -846,7 +867,7 @@ Q8Plan plan_q8(int64_t b, int64_t K, int64_t N) {
   const int64_t lds_a = (b * (K + kRowPad) + 1023) / 1024 * 1024;
   p.alds = lds_a <= kLdsLimbBudget;
   p.lds_a = p.alds ? int(lds_a) : 0;
-  p.rb = GP > 40 ? 1 : fit_rb(N, size_t(p.lds_a), scale_lds_bytes(16, int(G)) + 8 * size_t(p.nt) * 256, 8);
+  p.rb = GP > 40 ? 1 : fit_rb(N, 1, size_t(p.lds_a), scale_lds_bytes(16, int(G)) + 8 * size_t(p.nt) * 256, 8);
   p.rb = std::min(p.rb, 2);
   for (int pmax = b <= 4 ? 5 : 3;; ++pmax) {
     if (pmax > (p.alds ? kPmaxLds : (p.rb == 1 ? kQ8PmaxReg : kPmaxLds))) return p;  // not supported
@@ -916,7 +937,7 @@ void launch_q8_n(const Q8Plan &p, const Q8Args &a) {
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
   // two int8 limb planes [b, K + 16] and the per-token scales
-  return align256(size_t(limb_region_bytes(b, K))) + align256(16 * sizeof(float));
+  return align256(size_t(limb_region_bytes(b, K))) + align256(size_t(kGemvMaxTokens) * sizeof(float));
 }
 
 hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
@@ -940,7 +961,7 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
                             hipStream_t stream) {
   const GemvWs w = carve(const_cast<void *>(workspace), b, K);
   const GemvPlan p = plan_gemv(b, K, N);
-  const dim3 grid(unsigned((N + 16 * p.rb - 1) / (16 * p.rb)));
+  const dim3 grid(unsigned((N + 16 * p.rb - 1) / (16 * p.rb)), unsigned(p.chunks));
   const GemvArgs a{&w, b, K, N, packed, scales, y, y_dtype, stream};
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   if (p.kind == 0) launch_stream<true>(p, grid, a);

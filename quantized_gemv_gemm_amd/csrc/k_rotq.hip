@@ -77,8 +77,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void gemv_prep_x_kernel(
         const int hi = (q + 128) >> 8;  // floor division: lo lands in [-128, 127]
         const int64_t e = int64_t(blk) * kHBlock + lane + 64 * j;
         if (b > 8) {  // operand order (see limb_frag_offset)
-          xhi[limb_frag_offset(int(t), e, 0)] = (int8_t)hi;
-          xhi[limb_frag_offset(int(t), e, 1)] = (int8_t)(q - hi * 256);
+          xhi[limb_frag_offset(int(t), e, 0, K)] = (int8_t)hi;
+          xhi[limb_frag_offset(int(t), e, 1, K)] = (int8_t)(q - hi * 256);
         } else {
           hrow[e] = (int8_t)hi;
           lrow[e] = (int8_t)(q - hi * 256);

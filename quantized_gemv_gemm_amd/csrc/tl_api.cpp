@@ -107,13 +107,13 @@ int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs
 }
 
 size_t tl_gemv_workspace_size(int64_t b, int64_t K, int64_t N) {
-  if (b < 0 || b > 16 || K <= 0 || K % tl::kGroup || N < 0) return 0;
+  if (b < 0 || b > tl::kGemvMaxTokens || K <= 0 || K % tl::kGroup || N < 0) return 0;
   return tl::gemv_workspace_bytes(b, K, N);
 }
 
 namespace {
-int check_gemv_shape(int64_t b, int64_t K, int64_t N) {
-  if (b < 0 || b > 16 || N < 0 || K <= 0 || K % tl::kGroup || N >= kMaxDim || K >= kMaxDim)
+int check_gemv_shape(int64_t b, int64_t K, int64_t N, int64_t bmax = tl::kGemvMaxTokens) {
+  if (b < 0 || b > bmax || N < 0 || K <= 0 || K % tl::kGroup || N >= kMaxDim || K >= kMaxDim)
     return TL_ERR_SHAPE;
   return TL_OK;
 }
@@ -236,7 +236,7 @@ int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *s
 int tl_gemv_ternary_q8(const int8_t *xq, const float *tok_scale, int64_t b, int64_t K, int64_t N,
                        const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
                        void *stream) {
-  if (int s = check_gemv_shape(b, K, N)) return s;
+  if (int s = check_gemv_shape(b, K, N, tl::kTokChunk)) return s;
   if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
   if (b == 0 || N == 0) return TL_OK;
   if (!xq || !tok_scale || !packed || !scales || !y) return TL_ERR_NULLPTR;
@@ -292,6 +292,92 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
   if (any_alias(in, 5, out, 3)) return TL_ERR_ALIAS;
   return from_hip(tl::launch_gemm(xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype,
                                   acc_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// whole layer from the raw input, path chosen by the token count
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kLinCounters = 1024;  // the GEMM's split-K counters: kept at offset 0 for both paths
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct LinearLayout {
+  int path;
+  size_t gemm_ws;  // counters + partials (0: the GEMM runs unsplit)
+  size_t xq, sx;   // offsets of the int8 path's activations and token scales
+  size_t total;
+};
+
+LinearLayout linear_layout(int64_t T, int64_t K, int64_t N) {
+  LinearLayout l{};
+  l.path = tl_linear_path(T, K, N);
+  if (l.path == TL_PATH_GEMV) {
+    l.total = kLinCounters + tl::gemv_workspace_bytes(T, K, N);
+  } else {
+    l.gemm_ws = tl::gemm_workspace_bytes(T, K, N);
+    l.xq = align256(l.gemm_ws > kLinCounters ? l.gemm_ws : kLinCounters);
+    l.sx = l.xq + align256(size_t(T) * K);
+    l.total = l.sx + align256(size_t(T) * 4);
+  }
+  return l;
+}
+
+}  // namespace
+
+int tl_linear_path(int64_t T, int64_t K, int64_t N) {
+  (void)K;
+  if (T <= tl::kTokChunk) return TL_PATH_GEMV;
+  if (T > tl::kGemvMaxTokens) return TL_PATH_INT8;
+  // 17..64 tokens: the GEMV runs one chunk of 16 tokens per grid row, each
+  // streaming the weights again; it stays ahead while its workgroups (one per 64
+  // rows and chunk) fit in about 2.5 rounds of the 256 compute units.
+  const int64_t wg = tl::limb_chunks(T) * ((N + 63) / 64);
+  return wg <= 640 ? TL_PATH_GEMV : TL_PATH_INT8;
+}
+
+size_t tl_linear_workspace_size(int64_t T, int64_t K, int64_t N) {
+  if (T < 0 || N < 0 || K <= 0 || K % tl::kHBlock || T >= kMaxDim || N >= kMaxDim) return 0;
+  return linear_layout(T, K, N).total;
+}
+
+int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const int8_t *signs,
+                    const uint32_t *packed, const uint16_t *scales, const int8_t *q,
+                    const float *row_scale, void *y, int y_dtype, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  if (T < 0 || N < 0 || K <= 0 || K % tl::kHBlock || T >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return TL_ERR_SHAPE;
+  if (!tl::fused_input_supported(K)) return TL_ERR_UNSUPPORTED;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (T == 0 || N == 0) return TL_OK;
+  if (!x || !packed || !scales || !q || !row_scale || !y) return TL_ERR_NULLPTR;
+  const LinearLayout l = linear_layout(T, K, N);
+  if (!workspace || workspace_bytes < l.total) return TL_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(q) ||
+      !aligned16(row_scale) || !aligned16(y) || !aligned16(workspace) || (signs && !aligned16(signs)))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(T) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{x, size_t(T) * K * 2}, {signs, signs ? size_t(K) : 0u},
+               {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2},
+               {q, size_t(N) * G}, {row_scale, size_t(N) * 4}};
+  Span out[] = {{y, ysz}, {workspace, l.total}};
+  if (any_alias(in, 6, out, 2)) return TL_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *ws = static_cast<char *>(workspace);
+  if (l.path == TL_PATH_GEMV) {
+    void *gw = ws + kLinCounters;
+    hipError_t e = tl::launch_gemv_prepare_rotated(x, T, K, signs, gw, st);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(tl::launch_gemv_main(gw, T, K, N, packed, scales, y, y_dtype, st));
+  }
+  int8_t *xq = reinterpret_cast<int8_t *>(ws + l.xq);
+  float *sx = reinterpret_cast<float *>(ws + l.sx);
+  hipError_t e = tl::launch_quant_x(x, T, K, signs, xq, sx, st);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(tl::launch_gemm(xq, sx, T, K, N, packed, q, row_scale, y, y_dtype, nullptr,
+                                  l.gemm_ws ? workspace : nullptr, st));
 }
 
 }  // extern "C"

@@ -29,17 +29,24 @@ hipError_t launch_quant(const float *xr, int64_t T, int64_t K, int8_t *xq, float
 // Decode activation limbs in the GEMV workspace.  b <= 8: row-major rows, hi
 // limbs [b][K + 16] then lo limbs [b][K + 16].  b > 8: the operand order of
 // v_mfma_i32_16x16x64_i8, so that every operand load reads 1 KB contiguously:
-// for group g, 64-k half h and limb l, 64 lanes x 16 bytes, where lane
-// r + 16 q holds A row r (token 4 (r % 4) + r / 4) and k = 128 g + 32 q + 16 h + j.
+// tokens in chunks of 16 (chunk c = t / 16 owns 32 K bytes at 32 K c); inside a
+// chunk, for group g, 64-k half h and limb l, 64 lanes x 16 bytes, where lane
+// r + 16 q holds A row r (token 16 c + 4 (r % 4) + r / 4) and
+// k = 128 g + 32 q + 16 h + j.
 constexpr int kLimbRowPad = 16;
+constexpr int kTokChunk = 16;      // tokens per MFMA operand (and per GEMV grid row)
+constexpr int kGemvMaxTokens = 64; // decode tokens per call
+__host__ __device__ inline int64_t limb_chunks(int64_t b) { return (b + kTokChunk - 1) / kTokChunk; }
 __host__ __device__ inline int64_t limb_region_bytes(int64_t b, int64_t K) {
-  return b > 8 ? 32 * K : 2 * b * (K + kLimbRowPad);
+  return b > 8 ? 32 * K * limb_chunks(b) : 2 * b * (K + kLimbRowPad);
 }
-__host__ __device__ inline int64_t limb_frag_offset(int t, int64_t k, int limb) {
+__host__ __device__ inline int64_t limb_frag_offset(int t, int64_t k, int limb, int64_t K) {
   const int64_t g = k >> 7;
   const int kk = int(k & 127);
-  const int row = 4 * (t & 3) + (t >> 2);
-  return ((((g * 2 + ((kk >> 4) & 1)) * 2 + limb) * 64 + row + 16 * (kk >> 5)) << 4) + (kk & 15);
+  const int tc = t & (kTokChunk - 1);
+  const int row = 4 * (tc & 3) + (tc >> 2);
+  return 32 * K * (t / kTokChunk) +
+         (((((g * 2 + ((kk >> 4) & 1)) * 2 + limb) * 64 + row + 16 * (kk >> 5)) << 4) + (kk & 15));
 }
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t N);

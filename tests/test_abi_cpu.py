@@ -77,9 +77,11 @@ def test_gemv_rejections():
     L = tl.lib()
     ws = L.tl_gemv_workspace_size(4, 1024, 256)
     assert ws >= 2 * 4 * 1024
-    assert L.tl_gemv_workspace_size(17, 1024, 256) == 0
+    assert L.tl_gemv_workspace_size(65, 1024, 256) == 0
+    assert L.tl_gemv_workspace_size(64, 1024, 256) >= 2 * 64 * 1024
     args = lambda b=4, K=1024, N=256, y=FAKE4, dt=0, w=FAKE5, wb=ws: (FAKE, b, K, N, FAKE2, FAKE3, y, dt, w, wb, None)
-    assert L.tl_gemv_ternary(*args(b=17)) == 2
+    assert L.tl_gemv_ternary(*args(b=65)) == 2
+    assert L.tl_gemv_ternary(*args(b=64, wb=ws)) == 7   # 64 tokens need a larger workspace
     assert L.tl_gemv_ternary(*args(K=1000)) == 2
     assert L.tl_gemv_ternary(*args(dt=7)) == 4
     assert L.tl_gemv_ternary(*args(y=None)) == 1
@@ -147,7 +149,7 @@ def test_fused_input_rejections():
     ws = L.tl_gemv_workspace_size(4, 1024, 256)
     assert L.tl_gemv_prepare_x(FAKE, 4, 1536, None, FAKE2, ws, None) == 2          # K % 1024
     assert L.tl_gemv_prepare_x(FAKE, 4, 66560, None, FAKE2, 1 << 30, None) == 6    # K > 65536: unfused calls
-    assert L.tl_gemv_prepare_x(FAKE, 17, 1024, None, FAKE2, ws, None) == 2
+    assert L.tl_gemv_prepare_x(FAKE, 65, 1024, None, FAKE2, ws, None) == 2
     assert L.tl_gemv_prepare_x(None, 4, 1024, None, FAKE2, ws, None) == 1
     assert L.tl_gemv_prepare_x(FAKE, 4, 1024, None, FAKE2, ws - 1, None) == 7
     assert L.tl_gemv_prepare_x(FAKE, 4, 1024, ODD, FAKE2, ws, None) == 3
@@ -164,3 +166,38 @@ def test_fused_input_rejections():
     assert L.tl_quant_act_int8_x(FAKE, 3, 1024, None, FAKE2, ODD, None) == 3
     assert L.tl_quant_act_int8_x(FAKE, 3, 1024, None, FAKE, FAKE3, None) == 8
     assert L.tl_quant_act_int8_x(FAKE, 0, 1024, None, FAKE2, FAKE3, None) == 0
+
+
+def test_linear_path_rule():
+    """Up to 16 tokens the GEMV; 17..64 while ceil(T/16) ceil(N/64) <= 640; above 64 the int8 path."""
+    P = tl.linear_path
+    for T in (0, 1, 8, 16):
+        assert P(T, 5120, 34816) == tl.PATH_GEMV and P(T, 17408, 1 << 20) == tl.PATH_GEMV
+    assert P(64, 5120, 10240) == tl.PATH_GEMV      # 4 x 160 = 640 workgroups
+    assert P(64, 17408, 5120) == tl.PATH_GEMV
+    assert P(17, 5120, 20480) == tl.PATH_GEMV      # 2 x 320
+    assert P(17, 5120, 20544) == tl.PATH_INT8      # 2 x 321
+    assert P(32, 5120, 34816) == tl.PATH_INT8      # gate_up: 2 x 544
+    assert P(65, 1024, 64) == tl.PATH_INT8 and P(512, 5120, 10240) == tl.PATH_INT8
+
+
+def test_linear_rejections():
+    L = tl.lib()
+    ws = L.tl_linear_workspace_size(5, 1024, 256)
+    assert ws >= 1024 + L.tl_gemv_workspace_size(5, 1024, 256)
+    ws8 = L.tl_linear_workspace_size(100, 1024, 256)   # int8 path: counters, xq, tok_scale
+    assert ws8 >= 1024 + 100 * 1024 + 400
+    assert L.tl_linear_workspace_size(5, 1000, 256) == 0
+    W = ctypes.c_void_p(0xC0000000)
+    args = lambda T=5, K=1024, N=256, y=FAKE4, dt=0, w=W, wb=ws, qq=FAKE3: (
+        FAKE, T, K, N, None, FAKE2, ctypes.c_void_p(0x30000000), qq, FAKE5, y, dt, w, wb, None)
+    assert L.tl_linear_apply(*args(K=1152)) == 2
+    assert L.tl_linear_apply(*args(K=66560, wb=1 << 40)) == 6
+    assert L.tl_linear_apply(*args(dt=9)) == 4
+    assert L.tl_linear_apply(*args(qq=None)) == 1
+    assert L.tl_linear_apply(*args(w=None)) == 7
+    assert L.tl_linear_apply(*args(wb=ws - 1)) == 7
+    assert L.tl_linear_apply(*args(T=100, wb=ws)) == 7            # the int8 path needs more
+    assert L.tl_linear_apply(*args(y=ODD)) == 3
+    assert L.tl_linear_apply(*args(y=FAKE)) == 8
+    assert L.tl_linear_apply(*args(T=0)) == 0 and L.tl_linear_apply(*args(N=0)) == 0

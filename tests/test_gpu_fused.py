@@ -25,14 +25,14 @@ def _signs(K, seed):
 
 
 def _limb_region(b, K):
-    return 32 * K if b > 8 else 2 * b * (K + 16)
+    return 32 * K * ((b + 15) // 16) if b > 8 else 2 * b * (K + 16)
 
 
 def _limbs(ws, b, K):
     """hi and lo limb rows [b, K] and the token scales from a GEMV workspace: rows
-    K + 16 bytes apart for b <= 8; for b > 8 the matrix-core operand order (per
-    128-group, 64-k half and limb: 64 lanes x 16 bytes, lane = row + 16 (k%128)//32,
-    row = 4 (t % 4) + t // 4)."""
+    K + 16 bytes apart for b <= 8; for b > 8 the matrix-core operand order (chunks
+    of 16 tokens 32 K bytes apart; in a chunk, per 128-group, 64-k half and limb:
+    64 lanes x 16 bytes, lane = row + 16 (k%128)//32, row = 4 (t % 4) + (t % 16) // 4)."""
     a = ws.cpu().numpy()
     if b <= 8:
         Kp = K + 16
@@ -43,8 +43,9 @@ def _limbs(ws, b, K):
         g, kk = k // 128, k % 128
         hi, lo = np.empty((b, K), np.uint8), np.empty((b, K), np.uint8)
         for t in range(b):
-            row = 4 * (t % 4) + t // 4
-            base = (((g * 2 + (kk // 16) % 2) * 2) * 64 + row + 16 * (kk // 32)) * 16 + kk % 16
+            row = 4 * (t % 4) + (t % 16) // 4
+            base = 32 * K * (t // 16) + \
+                (((g * 2 + (kk // 16) % 2) * 2) * 64 + row + 16 * (kk // 32)) * 16 + kk % 16
             hi[t] = a[base]
             lo[t] = a[base + 64 * 16]
     off = (_limb_region(b, K) + 255) // 256 * 256
@@ -52,7 +53,8 @@ def _limbs(ws, b, K):
 
 
 @pytest.mark.parametrize("K,b,signed", [(1024, 1, False), (5120, 4, True), (5120, 16, False),
-                                        (17408, 1, True), (17408, 3, False), (33792, 2, True)])
+                                        (17408, 1, True), (17408, 3, False), (33792, 2, True),
+                                        (2048, 17, True), (5120, 40, False), (1024, 64, False)])
 def test_gemv_prepare_fused_bitexact(tl, K, b, signed):
     import torch
     d = dev()
@@ -79,7 +81,8 @@ def test_gemv_prepare_fused_bitexact(tl, K, b, signed):
     assert np.abs(v).max() <= 32639
 
 
-@pytest.mark.parametrize("K,N,b", [(5120, 1000, 1), (5120, 10240, 8), (17408, 512, 2)])
+@pytest.mark.parametrize("K,N,b", [(5120, 1000, 1), (5120, 10240, 8), (17408, 512, 2),
+                                   (5120, 1000, 33), (3072, 300, 64)])
 def test_gemv_ternary_fused_matches(tl, K, N, b):
     import torch
     d = dev()

@@ -203,7 +203,8 @@ def _gemv_case(tl, L, b, x_layer_cfg):
 
 
 @pytest.mark.parametrize("name,b", [("tiny", 1), ("qkv", 1), ("qkv", 4), ("qkv", 8), ("qkv", 16),
-                                    ("gate_up", 1), ("gate_up", 16), ("down", 1), ("down", 16)])
+                                    ("gate_up", 1), ("gate_up", 16), ("down", 1), ("down", 16),
+                                    ("qkv", 32), ("qkv", 64), ("down", 48)])
 def test_gemv_parity(tl, name, b):
     L = layer(name, tl)
     c, li, _, _ = SHAPES[name]
@@ -211,7 +212,8 @@ def test_gemv_parity(tl, name, b):
 
 
 @pytest.mark.parametrize("K,N,b", [(128, 300, 3), (256, 17, 16), (1024, 1000, 5), (3072, 64, 2),
-                                   (384, 33, 8), (17408, 48, 1), (5120, 100, 12)])
+                                   (384, 33, 8), (17408, 48, 1), (5120, 100, 12),
+                                   (256, 17, 17), (1024, 1000, 31), (384, 33, 50), (17408, 48, 64)])
 def test_gemv_ragged(tl, K, N, b):
     """N not a multiple of the row tile, K smaller than the wave count, odd b."""
     import torch
