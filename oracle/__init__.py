@@ -23,6 +23,8 @@ from .ternary import (  # noqa: F401
     sylvester_hadamard,
     rotate_exact,
     rotate_f32,
+    half_block_stage,
+    half_block_join,
     encode_words,
     decode_words,
     packed_size_words,

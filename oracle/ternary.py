@@ -74,6 +74,39 @@ def rotate_f32(x: np.ndarray, signs: np.ndarray | None = None) -> np.ndarray:
     return rotate_exact(x, signs).astype(np.float32)
 
 
+def half_block_stage(x_half: np.ndarray, signs_half: np.ndarray | None = None) -> np.ndarray:
+    """First stage of a 1024-block split in the middle by a K-shard boundary:
+    u = H512 (d * x_half) for the 512 columns one rank holds, without the 1/32.
+
+    [P1] §1: down_proj's 17408 inputs split over two GPUs at 8704, the middle of a
+    block; by H1024 [a; b] = [H512 a + H512 b; H512 a - H512 b] each rank
+    transforms only its own half and the halves are exchanged.
+    x_half: [T, 512]; signs_half: [512] of +-1 or None.  Dense, binary64 (exact for
+    the generator's inputs, as in rotate_exact).
+    """
+    x = np.asarray(x_half, dtype=np.float64)
+    if x.ndim != 2 or x.shape[1] != HBLOCK // 2:
+        raise ValueError("x_half must be [T, 512]")
+    d = np.ones(HBLOCK // 2) if signs_half is None else np.asarray(signs_half, dtype=np.float64)
+    return (x * d) @ sylvester_hadamard(HBLOCK // 2).T
+
+
+def half_block_join(u_lo: np.ndarray, u_hi: np.ndarray, half: int) -> np.ndarray:
+    """Second stage: the rotated values of one half of the split block from both
+    halves' stage results, rounded once to float32.
+
+    [P1] §1: the rank holding the first half keeps the sum, the other the
+    difference.  half 0: (u_lo + u_hi)/32, half 1: (u_lo - u_hi)/32, where u_lo
+    and u_hi are the stages of the block's first and second 512 columns.
+    """
+    if half not in (0, 1):
+        raise ValueError("half must be 0 or 1")
+    u_lo = np.asarray(u_lo, dtype=np.float64)
+    u_hi = np.asarray(u_hi, dtype=np.float64)
+    v = u_lo + u_hi if half == 0 else u_lo - u_hi
+    return (v / 32.0).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # packed 2-bit codes  ([P1] "前提": 2-bit representation of {-1, 0, +1})
 # ---------------------------------------------------------------------------

@@ -146,6 +146,70 @@ def test_rotation_rank_swap_control():
     assert abs(oracle.rel_fro(swapped, ref) - np.sqrt(2.0)) < 1e-12
 
 
+def check_half_block(stage, join):
+    """The split-block stages reproduce the unsplit rotation bit for bit."""
+    rng = np.random.default_rng(5)
+    T = 3
+    mant = rng.integers(128, 256, (T, 1024))
+    expo = rng.integers(-24, 1, (T, 1024))
+    x = np.ldexp(mant.astype(np.float64), expo) * np.where(rng.random((T, 1024)) < .5, -1, 1)
+    d = np.where(rng.random(1024) < 0.5, -1.0, 1.0)
+    for signs in (None, d):
+        lo = stage(x[:, :512], None if signs is None else signs[:512])
+        hi = stage(x[:, 512:], None if signs is None else signs[512:])
+        got = np.concatenate([join(lo, hi, 0), join(lo, hi, 1)], axis=1)
+        np.testing.assert_array_equal(got, oracle.rotate_f32(x, signs))
+    # closed form of the stage: a unit vector e_m gives (-1)^popcount(i & m), no 1/32
+    for m in (0, 1, 300, 511):
+        e = np.zeros((1, 512))
+        e[0, m] = 1.0
+        want = np.array([(-1.0) ** bin(i & m).count("1") for i in range(512)])
+        np.testing.assert_array_equal(stage(e)[0], want)
+
+
+def test_half_block_pins():
+    check_half_block(oracle.half_block_stage, oracle.half_block_join)
+
+
+def _join_swapped(u_lo, u_hi, half):
+    """Mutant: the ranks' sum and difference exchanged ([P1] §1's deliberate swap)."""
+    return oracle.half_block_join(u_lo, u_hi, 1 - half)
+
+
+def _stage_scaled(x_half, signs_half=None):
+    """Mutant: the 1/32 applied in the stage as well."""
+    return oracle.half_block_stage(x_half, signs_half) / 32.0
+
+
+@pytest.mark.parametrize("stage,join", [(oracle.half_block_stage, _join_swapped),
+                                        (_stage_scaled, oracle.half_block_join)])
+def test_half_block_mutants_fail(stage, join):
+    with pytest.raises(AssertionError):
+        check_half_block(stage, join)
+
+
+def test_sharded_layer_matches_unsplit():
+    """Two K-shards split inside a block ([P1] §1's TP=2 layout at K = 2048,
+    boundary 1536): each rank rotates its full blocks and its half block, the
+    halves are joined, and the partial outputs add up to the unsplit layer."""
+    rng = np.random.default_rng(6)
+    T, K, N, cut = 2, 2048, 40, 1536
+    x = rng.integers(-512, 512, (T, K)) / 256.0
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    xr0 = np.empty((T, cut), np.float32)
+    xr0[:, :1024] = oracle.rotate_f32(x[:, :1024])
+    u_lo = oracle.half_block_stage(x[:, 1024:1536])
+    u_hi = oracle.half_block_stage(x[:, 1536:2048])
+    xr0[:, 1024:] = oracle.half_block_join(u_lo, u_hi, 0)
+    xr1 = oracle.half_block_join(u_lo, u_hi, 1)
+    np.testing.assert_array_equal(np.concatenate([xr0, xr1], axis=1), oracle.rotate_f32(x))
+    y = (oracle.gemv_ternary(xr0, codes[:, :cut], scales[:, :cut // 128]) +
+         oracle.gemv_ternary(xr1, codes[:, cut:], scales[:, cut // 128:]))
+    ref = oracle.gemv_ternary(oracle.rotate_f32(x), codes, scales)
+    assert oracle.rel_fro(y, ref) < 1e-13
+
+
 # ---------------------------------------------------------------------------
 # packing
 # ---------------------------------------------------------------------------
