@@ -323,6 +323,14 @@ def main():
     prep_ms = {b: [run_time(lambda: tl.gemv_prepare_x(x_dec[b], ws_dec[b]))] for b in DECODE_BS}
     quant_ms = {k: [run_time(lambda: tl.quant_act_int8_x(P["x"], xq=P["xq"], tok_scale=P["sx"]))]
                 for k, P in pre.items()}
+    # split-block rotation stages of a TP=2 shard boundary (down_proj's block 8):
+    # the half stage on a column slice of the raw input, the join into the rank's columns
+    split_us = {}
+    for T, xs in ((16, x_dec[16]), (PREFILL_M, pre["down"]["x"])):
+        u = torch.empty((T, 512), dtype=torch.float64, device=dev)
+        xr_half = torch.empty((T, 512), dtype=torch.float32, device=dev)
+        split_us[f"half_T{T}"] = round(run_time(lambda: tl.hadamard_half(xs[:, 512:1024], u=u)) * 1e3, 2)
+        split_us[f"join_T{T}"] = round(run_time(lambda: tl.hadamard_join(u, u, 1, out=xr_half)) * 1e3, 2)
     gc.enable()
 
     if os.environ.get("BENCH_DEBUG"):
@@ -395,7 +403,8 @@ def main():
         "decode_gemv_by_b": by_b,
         "input_kernels_us": {
             "decode_rotate_prep": {str(b): round(float(np.mean(prep_ms[b])) * 1e3, 2) for b in DECODE_BS},
-            "prefill_rotate_quant_m512": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in quant_ms.items()}},
+            "prefill_rotate_quant_m512": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in quant_ms.items()},
+            "split_block_stages": split_us},
         "prefill_tops": round(pre_tops, 1),
         "prefill_gemm": pre_out,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

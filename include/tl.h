@@ -129,6 +129,35 @@ int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs
                     void *stream);
 
 /*
+ * tl_hadamard_half, tl_hadamard_join -- the rotation of a 1024-block that a
+ * K-shard boundary splits in the middle, in two stages with an exchange of the
+ * stage results between the two ranks in between.
+ *   [P1] "1. TP=2 への移植" (17408 / 2 = 8704 falls in the middle of a block;
+ *   H1024 [a; b] = [H512 a + H512 b; H512 a - H512 b]: each rank transforms its
+ *   own 512 columns, the results are exchanged, the rank with the first half
+ *   keeps the sum, the other the difference).
+ * tl_hadamard_half:
+ * in  x      bf16 [T, 512] with rows ldx elements apart (ldx >= 512, ldx % 8 == 0,
+ *            so a column slice of the rank's [T, K_shard] input can be passed)
+ * in  signs  int8 [512] of +-1 for these columns, or NULL for all +1
+ * out u      f64  [T, 512] dense: u[t, i] = sum_m (-1)^popcount(i & m) d[m] x[t, m]
+ *            (no 1/32), exact in binary64 for inputs that are multiples of 2^-31
+ *            below 2^8 in magnitude (bf16 with |x| >= 2^-24).
+ * tl_hadamard_join:
+ * in  u_lo, u_hi  f64 [T, 512]: the stage results of the block's first and second
+ *            512 columns (one computed here, one received from the other rank)
+ * in  half   0 for the rank that holds the first half, 1 for the other
+ * out xr     f32 [T, 512] with rows ldxr elements apart (ldxr >= 512, ldxr % 4 == 0):
+ *            half 0: fl32((u_lo + u_hi) / 32), half 1: fl32((u_lo - u_hi) / 32) --
+ *            bit for bit the columns tl_hadamard_blk produces for that half.
+ * The exchange itself (512 binary64 values per token each way) is the caller's.
+ */
+int tl_hadamard_half(const uint16_t *x, int64_t T, int64_t ldx, const int8_t *signs, double *u,
+                     void *stream);
+int tl_hadamard_join(const double *u_lo, const double *u_hi, int64_t T, int half, float *xr,
+                     int64_t ldxr, void *stream);
+
+/*
  * tl_gemv_ternary -- decode GEMV, y = W xr for 1..64 tokens.
  *   [P1] "前提" (y = W (H_blk x), W = code * group scale).
  * in  xr      f32    [b, K]      rotated activations (tl_hadamard_blk output)

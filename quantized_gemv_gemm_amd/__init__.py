@@ -35,6 +35,8 @@ _SIGS = {
     "tl_packed_bytes": (_c_sz, [_c_i64, _c_i64]),
     "tl_pack_weights": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "tl_hadamard_blk": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "tl_hadamard_half": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "tl_hadamard_join": (ctypes.c_int, [_c_p, _c_p, _c_i64, ctypes.c_int, _c_p, _c_i64, _c_p]),
     "tl_gemv_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "tl_gemv_ternary": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, ctypes.c_int,
                                        _c_p, _c_sz, _c_p]),
@@ -453,4 +455,50 @@ def linear_apply(x, packed, scales, q, row_scale, signs=None, out_dtype=None, ou
     _check("tl_linear_apply", lib().tl_linear_apply(
         _ptr(x), T, K, N, _ptr(signs), _ptr(packed), _ptr(scales), _ptr(q), _ptr(row_scale), _ptr(out), code,
         _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def _need_rows(t, name, dtype, cols):
+    """A 2-D device tensor of ``cols`` contiguous columns whose rows may be further apart."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype or t.dim() != 2 or t.shape[1] != cols or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a {dtype} [T, {cols}] view with unit column stride")
+
+
+def hadamard_half(x, signs=None, u=None):
+    """First split-block stage: x bf16 [T,512] (rows may be a column slice of a wider
+    input) -> u f64 [T,512] = H512 (d * x), exact, no 1/32."""
+    import torch
+    _need_rows(x, "x", torch.bfloat16, 512)
+    if signs is not None:
+        _need(signs, "signs", torch.int8, 1)
+        if signs.shape != (512,):
+            raise ValueError("signs must be [512]")
+    T = x.shape[0]
+    u = torch.empty((T, 512), dtype=torch.float64, device=x.device) if u is None else u
+    _need(u, "u", torch.float64, 2)
+    if u.shape != (T, 512):
+        raise ValueError("u must be [T, 512]")
+    _check("tl_hadamard_half", lib().tl_hadamard_half(_ptr(x), T, x.stride(0) if T > 1 else 512, _ptr(signs),
+                                                      _ptr(u), _stream(x.device)))
+    return u
+
+
+def hadamard_join(u_lo, u_hi, half, out=None):
+    """Second split-block stage: the rank's 512 rotated columns, f32 [T,512]
+    (``out`` may be a column slice of the rank's rotated input)."""
+    import torch
+    _need(u_lo, "u_lo", torch.float64, 2)
+    _need(u_hi, "u_hi", torch.float64, 2)
+    T = u_lo.shape[0]
+    if u_lo.shape != (T, 512) or u_hi.shape != (T, 512):
+        raise ValueError("u_lo and u_hi must be [T, 512]")
+    out = torch.empty((T, 512), dtype=torch.float32, device=u_lo.device) if out is None else out
+    _need_rows(out, "out", torch.float32, 512)
+    if out.shape[0] != T:
+        raise ValueError("out must have T rows")
+    _check("tl_hadamard_join", lib().tl_hadamard_join(_ptr(u_lo), _ptr(u_hi), T, int(half), _ptr(out),
+                                                      out.stride(0) if T > 1 else 512, _stream(u_lo.device)))
     return out

@@ -106,6 +106,33 @@ int tl_hadamard_blk(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs
   return from_hip(tl::launch_hadamard(x, T, K, signs, xr, static_cast<hipStream_t>(stream)));
 }
 
+int tl_hadamard_half(const uint16_t *x, int64_t T, int64_t ldx, const int8_t *signs, double *u,
+                     void *stream) {
+  if (T < 0 || T >= kMaxDim || ldx < tl::kHBlock / 2 || ldx >= kMaxDim) return TL_ERR_SHAPE;
+  if (T == 0) return TL_OK;
+  if (!x || !u) return TL_ERR_NULLPTR;
+  if (!aligned16(x) || ldx % 8 || !aligned16(u)) return TL_ERR_ALIGN;
+  const size_t half = tl::kHBlock / 2;
+  Span in[] = {{x, (size_t(T - 1) * ldx + half) * 2}, {signs, signs ? half : 0u}};
+  Span out[] = {{u, size_t(T) * half * 8}};
+  if (any_alias(in, 2, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_hadamard_half(x, T, ldx, signs, u, static_cast<hipStream_t>(stream)));
+}
+
+int tl_hadamard_join(const double *u_lo, const double *u_hi, int64_t T, int half, float *xr,
+                     int64_t ldxr, void *stream) {
+  if (T < 0 || T >= kMaxDim || ldxr < tl::kHBlock / 2 || ldxr >= kMaxDim || (half != 0 && half != 1))
+    return TL_ERR_SHAPE;
+  if (T == 0) return TL_OK;
+  if (!u_lo || !u_hi || !xr) return TL_ERR_NULLPTR;
+  if (!aligned16(u_lo) || !aligned16(u_hi) || !aligned16(xr) || ldxr % 4) return TL_ERR_ALIGN;
+  const size_t hb = tl::kHBlock / 2;
+  Span in[] = {{u_lo, size_t(T) * hb * 8}, {u_hi, size_t(T) * hb * 8}};
+  Span out[] = {{xr, (size_t(T - 1) * ldxr + hb) * 4}};
+  if (any_alias(in, 2, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_hadamard_join(u_lo, u_hi, T, half, xr, ldxr, static_cast<hipStream_t>(stream)));
+}
+
 size_t tl_gemv_workspace_size(int64_t b, int64_t K, int64_t N) {
   if (b < 0 || b > tl::kGemvMaxTokens || K <= 0 || K % tl::kGroup || N < 0) return 0;
   return tl::gemv_workspace_bytes(b, K, N);

@@ -72,6 +72,12 @@ hipError_t launch_gemv_q8(const int8_t *xq, const float *tok_scale, int64_t b, i
                           const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
                           hipStream_t stream);
 
+// split-block rotation stages (k_split.hip)
+hipError_t launch_hadamard_half(const uint16_t *x, int64_t T, int64_t ldx, const int8_t *signs,
+                                double *u, hipStream_t stream);
+hipError_t launch_hadamard_join(const double *u_lo, const double *u_hi, int64_t T, int half, float *xr,
+                                int64_t ldxr, hipStream_t stream);
+
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
                        const uint32_t *packed, const int8_t *q, const float *row_scale, void *y,

@@ -201,3 +201,19 @@ def test_linear_rejections():
     assert L.tl_linear_apply(*args(y=ODD)) == 3
     assert L.tl_linear_apply(*args(y=FAKE)) == 8
     assert L.tl_linear_apply(*args(T=0)) == 0 and L.tl_linear_apply(*args(N=0)) == 0
+
+
+def test_split_block_rejections():
+    L = tl.lib()
+    assert L.tl_hadamard_half(FAKE, 2, 500, None, FAKE2, None) == 2          # ldx < 512
+    assert L.tl_hadamard_half(FAKE, 2, 8704, None, None, None) == 1
+    assert L.tl_hadamard_half(FAKE, 2, 8700, None, FAKE2, None) == 3         # rows not 16-byte aligned
+    assert L.tl_hadamard_half(FAKE, 2, 8704, None, ODD, None) == 3
+    assert L.tl_hadamard_half(FAKE, 2, 512, None, FAKE, None) == 8
+    assert L.tl_hadamard_half(FAKE, 0, 512, None, FAKE2, None) == 0
+    assert L.tl_hadamard_join(FAKE, FAKE2, 2, 2, FAKE3, 512, None) == 2       # half must be 0 or 1
+    assert L.tl_hadamard_join(FAKE, FAKE2, 2, 0, FAKE3, 100, None) == 2
+    assert L.tl_hadamard_join(FAKE, None, 2, 0, FAKE3, 512, None) == 1
+    assert L.tl_hadamard_join(FAKE, FAKE2, 2, 1, FAKE3, 514, None) == 3
+    assert L.tl_hadamard_join(FAKE, FAKE2, 2, 1, FAKE2, 512, None) == 8
+    assert L.tl_hadamard_join(FAKE, FAKE2, 0, 1, FAKE3, 512, None) == 0
