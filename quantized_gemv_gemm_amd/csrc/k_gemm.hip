@@ -30,11 +30,15 @@
 // Work distribution: the tiles are dealt out in whole rounds of kSlots
 // workgroups (one per compute unit), each round XCD-aware so that the four
 // M-blocks of one weight strip run on one XCD and share its L2.  The tiles left
-// over for a last, partial round are split along K into S pieces; every piece
-// stores its int32 partial tile to the workspace and bumps the tile's counter,
-// and the piece that arrives last adds the others and runs the epilogue
-// (integer sums: exact and order independent).  No workgroup ever waits for
-// another.
+// over for a last, partial round are either
+//  * cut into eight 32 x 128 sub-tiles (when at most kSlots / 8 are left), each a
+//    workgroup of its own over the whole K: the same pipeline with one 32 x 32
+//    MFMA tile per wave; nothing to add up afterwards; or
+//  * split along K into S pieces; every piece stores its int32 partial tile to
+//    the workspace and bumps the tile's counter, and the piece that arrives last
+//    adds the others and runs the epilogue (integer sums: exact and order
+//    independent).
+// No workgroup ever waits for another.
 #include <algorithm>
 
 #include "tl_device.h"
@@ -46,34 +50,48 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 256;
 constexpr int kThreads = 256;
 constexpr int kPairK = 2 * kGroup;        // k per pipeline stage: one pair of groups
 constexpr int kAStride = kPairK + 16;     // LDS row pitch in bytes (padding spreads banks)
-constexpr int kABuf = kBM * kAStride;     // one activation stage in LDS
 constexpr int kSlots = 256;               // workgroups per round: the compute units of gfx950
 constexpr int kXcds = 8;                  // workgroup i runs on XCD i % 8
 constexpr int kMaxSplit = 6;
-constexpr int kTileInts = kBM * kBN;
 
-static_assert(kBM * kPairK == kThreads * 8 * 16, "A stage = 8 x 16 bytes per thread");
-static_assert(kBN == 4 * 64, "4 waves x 64 columns");
+// A workgroup tile of 32 MT x 128 J: each of the 4 waves owns all 32 MT rows and
+// 32 J columns (MT x J MFMA tiles of 32 x 32).
+template <int MT, int J>
+struct Tile {
+  static constexpr int BM = 32 * MT, BN = 4 * 32 * J;
+  static constexpr int ABuf = BM * kAStride;  // one activation stage in LDS
+  static constexpr int APieces = 2 * MT;      // 16-byte activation pieces per thread and pair
+  static constexpr int Ints = BM * BN;
+  static_assert(BM * kPairK == kThreads * APieces * 16, "A stage = APieces x 16 bytes per thread");
+};
+typedef Tile<4, 2> Big;     // 128 x 256: the tile of the whole rounds
+typedef Tile<1, 1> Narrow;  // 32 x 128: an eighth of a big tile, for a short last round
+constexpr int kBM = Big::BM;
+constexpr int kBN = Big::BN;
+constexpr int kABuf = Big::ABuf;
+constexpr int kTileInts = Big::Ints;
+constexpr int kNarrowPerTile = (Big::BM / Narrow::BM) * (Big::BN / Narrow::BN);
+
 static_assert(kTileInts == kThreads * 128, "128 accumulators per thread");
 
+template <int J>
 struct BStage {
-  v4u w[2][2];  // [N tile][lane quarter 2h, 2h+1]: tile words for both groups of the pair
-  int q[2][2];  // [N tile][group of the pair], as loaded
+  v4u w[J][2];  // [N tile][lane quarter 2h, 2h+1]: tile words for both groups of the pair
+  int q[J][2];  // [N tile][group of the pair], as loaded
   uint32_t keep[2];  // per group of the pair: all ones, or 0 for a padding pair / missing group
 };
 
 struct Schedule {
   int mb;         // M-blocks
   int tiles;      // MB * N-strips
-  int full;       // tiles computed whole, in rounds of kSlots (the rest are split)
-  int split;      // pieces per left-over tile (1: nothing is split)
-  int64_t left() const { return split > 1 ? tiles - full : 0; }
-  int64_t grid() const { return full + left() * split; }
+  int full;       // tiles computed whole, in rounds of kSlots (the rest are split or cut)
+  int split;      // pieces per left-over tile along K (1: nothing is split)
+  int narrow;     // 1: the left-over tiles are cut into kNarrowPerTile sub-tiles
+  int64_t left() const { return split > 1 || narrow ? tiles - full : 0; }
+  int64_t grid() const { return full + left() * (narrow ? kNarrowPerTile : split); }
 };
 
 __device__ __forceinline__ uint32_t perm_table(int qv) {
@@ -95,28 +113,31 @@ __device__ __forceinline__ v4i expand_word(uint32_t w, uint32_t table) {
 // buffer resources that cover exactly the tile's rows of xq, its packed row
 // blocks and its q rows: a read past M, past N or past the last group returns
 // zeros, which only ever meets zero weights or results that are not stored.
+template <int J>
 struct Frame {
   __amdgpu_buffer_rsrc_t ra, rb, rq;
   int aoff;       // byte offset of this thread's first staged activation piece
   int astep;      // 16 rows of activations, in bytes
   int adst;       // LDS offset of the first piece; piece i is 16 rows further
-  int boff[2];    // this lane's 16 bytes of the first tile of its weight column, per N tile
-  int qoff[2];    // q row of that column
+  int boff[J];    // this lane's 16 bytes of the first tile of its weight column, per N tile
+  int qoff[J];    // q row of that column
   int G;
 };
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 constexpr int kCoherent = 16;           // cache policy sc1: coherent across the XCDs' L2s
 
-__device__ __forceinline__ void load_a(v4u (&a)[8], const Frame &f, int p) {
+template <int NP, int J>
+__device__ __forceinline__ void load_a(v4u (&a)[NP], const Frame<J> &f, int p) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NP; ++i)
     a[i] = __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.aoff, p * kPairK + i * f.astep, 0);
 }
 
-__device__ __forceinline__ void load_b(BStage &b, const Frame &f, int p, bool live) {
+template <int J>
+__device__ __forceinline__ void load_b(BStage<J> &b, const Frame<J> &f, int p, bool live) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < J; ++j) {
     b.w[j][0] = __builtin_amdgcn_raw_buffer_load_b128(f.rb, f.boff[j], p * 1024, 0);
     b.w[j][1] = __builtin_amdgcn_raw_buffer_load_b128(f.rb, f.boff[j] + 256, p * 1024, 0);
     b.q[j][0] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(f.rq, f.qoff[j], 2 * p, 0);
@@ -129,33 +150,37 @@ __device__ __forceinline__ void load_b(BStage &b, const Frame &f, int p, bool li
   b.keep[1] = live && 2 * p + 1 < f.G ? ~0u : 0u;
 }
 
-__device__ __forceinline__ void store_a(int8_t *buf, const v4u (&a)[8], const Frame &f) {
+template <int NP, int J>
+__device__ __forceinline__ void store_a(int8_t *buf, const v4u (&a)[NP], const Frame<J> &f) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<v4u *>(buf + f.adst + 16 * kAStride * i) = a[i];
+  for (int i = 0; i < NP; ++i) *reinterpret_cast<v4u *>(buf + f.adst + 16 * kAStride * i) = a[i];
 }
 
 // k-step s (0..7) of a pair: group gi = s / 4, sub-step ss = s % 4.  Word 4h + ss
 // of the lane's column in group gi: words 4h, 4h+1 sit in the lane-quarter 2h slot
 // of the tile, 4h+2, 4h+3 in the 2h+1 slot.
-__device__ __forceinline__ void fetch_a(v4i (&af)[4], const int8_t *abase, int s) {
+template <int MT>
+__device__ __forceinline__ void fetch_a(v4i (&af)[MT], const int8_t *abase, int s) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
     af[mt] = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + kGroup * (s >> 2) + 16 * (s & 3));
 }
 
-__device__ __forceinline__ void fetch_b(v4i (&bf)[2], const BStage &b, int s) {
+template <int J>
+__device__ __forceinline__ void fetch_b(v4i (&bf)[J], const BStage<J> &b, int s) {
   const int gi = s >> 2, ss = s & 3;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < J; ++j)
     bf[j] = expand_word(b.w[j][ss >> 1][2 * gi + (ss & 1)], perm_table(b.q[j][gi]) & b.keep[gi]);
 }
 
-__device__ __forceinline__ void mfma_step(const v4i (&af)[4], const v4i (&bf)[2], v16i (&acc)[4][2]) {
+template <int MT, int J>
+__device__ __forceinline__ void mfma_step(const v4i (&af)[MT], const v4i (&bf)[J], v16i (&acc)[MT][J]) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[0], acc[mt][0], 0, 0, 0);
-    acc[mt][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[1], acc[mt][1], 0, 0, 0);
-  }
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      acc[mt][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[j], acc[mt][j], 0, 0, 0);
 }
 
 // One pair p.  Weight ring slot S = (p - p0) mod 4 is fixed at compile time; the
@@ -165,15 +190,16 @@ __device__ __forceinline__ void mfma_step(const v4i (&af)[4], const v4i (&bf)[2]
 // of p+3, and the ring holds (or is loading) pairs p+1..p+3.  On exit the same
 // holds for p+1.  Pairs before k0 are padding
 // (zero weights), data indices are clamped into [k0, k1).
-template <int S>
-__device__ __forceinline__ void pair_body(int p, int k0, int plast, int &lb, const Frame &f,
-                                          int8_t *lds, const int8_t *aread, BStage (&ring)[4],
-                                          v4u (&anext)[2][8], v4i (&af)[2][4], v4i (&bf)[2][2],
-                                          v16i (&acc)[4][2]) {
+template <int S, int MT, int J>
+__device__ __forceinline__ void pair_body(int p, int k0, int plast, int &lb, const Frame<J> &f,
+                                          int8_t *lds, const int8_t *aread, BStage<J> (&ring)[4],
+                                          v4u (&anext)[2][Tile<MT, J>::APieces], v4i (&af)[2][MT],
+                                          v4i (&bf)[2][J], v16i (&acc)[MT][J]) {
   constexpr int S1 = (S + 1) % 4;
+  constexpr int AB = Tile<MT, J>::ABuf;
   const int lb1 = lb == 2 ? 0 : lb + 1, lb2 = lb1 == 2 ? 0 : lb1 + 1;
-  const int8_t *cur = aread + lb * kABuf;
-  const int8_t *nxt = aread + lb1 * kABuf;
+  const int8_t *cur = aread + lb * AB;
+  const int8_t *nxt = aread + lb1 * AB;
   // Scheduling fences keep the issue order: LDS reads for k-step s+1, then the
   // MFMAs of k-step s interleaved with the expansion for s+1, then stage traffic.
 #pragma unroll
@@ -189,13 +215,13 @@ __device__ __forceinline__ void pair_body(int p, int k0, int plast, int &lb, con
     else
       fetch_b(bf[0], ring[S1], 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MT * J; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
     }
     __builtin_amdgcn_sched_barrier(0);
     if (s == 3) {
-      store_a(lds + lb2 * kABuf, anext[S & 1], f);
+      store_a(lds + lb2 * AB, anext[S & 1], f);
       load_a(anext[S & 1], f, min(max(p + 4, k0), plast));
     }
     if (s == 7) load_b(ring[S], f, min(max(p + 4, k0), plast), p + 4 >= k0);
@@ -215,17 +241,17 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // each 32x32 tile, rows 8*(r/4) + 4*h + r%4: four consecutive rows per r/4, whose
 // token scales come from LDS in one 16-byte read.  A tile that lies inside
 // [M, N] takes the variant without per-element bounds tests.
-template <bool kCheck, bool kF32>
-__device__ __forceinline__ void epilogue(const v16i (&acc)[4][2], const float *s_tok,
-                                         const float (&rsv)[2], int64_t m0, int64_t n0, int64_t M,
+template <bool kCheck, bool kF32, int MT, int J>
+__device__ __forceinline__ void epilogue(const v16i (&acc)[MT][J], const float *s_tok,
+                                         const float (&rsv)[J], int64_t m0, int64_t n0, int64_t M,
                                          int64_t N, int wave, int l32, int h, void *y,
                                          int32_t *acc_out) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + 64 * wave + 32 * j + l32;
+  for (int j = 0; j < J; ++j) {
+    const int64_t n = n0 + 32 * J * wave + 32 * j + l32;
     if (kCheck && n >= N) continue;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
         const int row = 32 * mt + 8 * rq + 4 * h;
@@ -251,21 +277,22 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[4][2], const float *s
 // activation buffers, free once the K loop is done) so that every lane stores 16
 // contiguous bytes of a row -- a wave writes whole rows -- instead of 2- or
 // 4-byte pieces down a column.  f32 output goes in two passes of 64 rows.
-template <bool kF32>
-__device__ __forceinline__ void epilogue_lds(const v16i (&acc)[4][2], const float *s_tok,
-                                             const float (&rsv)[2], int64_t m0, int64_t n0, int64_t N,
+template <bool kF32, int MT, int J>
+__device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const float *s_tok,
+                                             const float (&rsv)[J], int64_t m0, int64_t n0, int64_t N,
                                              int wave, int l32, int h, int tid, void *y, int8_t *stage) {
+  constexpr int BM = Tile<MT, J>::BM, BN = Tile<MT, J>::BN;
   constexpr int ES = kF32 ? 4 : 2;         // bytes per output
-  constexpr int PITCH = kBN * ES + 16;     // LDS row pitch (the pad spreads the 4-row steps over banks)
-  constexpr int ROWS = kF32 ? 64 : 128;    // rows per pass
-  constexpr int CPR = kBN * ES / 16;       // 16-byte chunks per row
+  constexpr int PITCH = BN * ES + 16;      // LDS row pitch (the pad spreads the 4-row steps over banks)
+  constexpr int ROWS = BM * PITCH <= 3 * kABuf ? BM : BM / 2;  // rows per pass
+  constexpr int CPR = BN * ES / 16;        // 16-byte chunks per row
   static_assert(ROWS * PITCH <= 3 * kABuf, "staging fits the activation buffers");
   __syncthreads();  // every wave is done with the activation buffers
 #pragma unroll
-  for (int pass = 0; pass < kBM / ROWS; ++pass) {
+  for (int pass = 0; pass < BM / ROWS; ++pass) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = 64 * wave + 32 * j + l32;
+    for (int j = 0; j < J; ++j) {
+      const int c = 32 * J * wave + 32 * j + l32;
 #pragma unroll
       for (int mt = pass * (ROWS / 32); mt < (pass + 1) * (ROWS / 32); ++mt)
 #pragma unroll
@@ -291,7 +318,7 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[4][2], const floa
       *reinterpret_cast<v4u *>(ybase + (int64_t(r) * N) * ES + 16 * cc) =
           *reinterpret_cast<const v4u *>(stage + r * PITCH + 16 * cc);
     }
-    if (pass + 1 < kBM / ROWS) __syncthreads();  // the next pass overwrites the staging rows
+    if (pass + 1 < BM / ROWS) __syncthreads();  // the next pass overwrites the staging rows
   }
 }
 
@@ -299,8 +326,16 @@ inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   Schedule sc;
   sc.mb = int((M + kBM - 1) / kBM);
   sc.tiles = sc.mb * int((N + kBN - 1) / kBN);
+  sc.narrow = 0;
   const int left = sc.tiles % kSlots;
   int best = 1;
+  if (left && left * kNarrowPerTile <= kSlots) {
+    // a short last round: every left-over tile becomes eight sub-tile workgroups
+    sc.narrow = 1;
+    sc.split = 1;
+    sc.full = sc.tiles - left;
+    return sc;
+  }
   if (left) {
     int64_t best_cost = (GP + 3) / 4 * 4;
     for (int S = 2; S <= kMaxSplit && S * left <= kSlots && S <= GP; ++S) {
@@ -314,6 +349,168 @@ inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   return sc;
 }
 
+struct GemmArgs {
+  const int8_t *xq;
+  const float *tok_scale;
+  int64_t M, K, N;
+  const uint32_t *packed;
+  const int8_t *q;
+  const float *row_scale;
+  void *y;
+  int y_dtype;
+  int32_t *acc_out, *part, *counters;
+};
+
+// One workgroup tile of 32 MT x 128 J at (m0, n0) over the pairs [k0, k1).  A
+// piece of a K-split tile (piece >= 0, big tiles only) publishes its partial
+// tile and only the last piece to arrive runs the epilogue.
+template <int MT, int J>
+__device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, int8_t *sA, float *s_tok,
+                                         int *s_last, int64_t m0, int64_t n0, int k0, int k1, int tile,
+                                         int piece, int slot) {
+  typedef Tile<MT, J> T;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t M = a.M, K = a.K, N = a.N;
+  const int G = int(K / kGroup);
+  const int GP = (G + 1) / 2;
+
+  Frame<J> f;
+  f.G = G;
+  {
+    const int64_t rows = M - m0 < T::BM ? M - m0 : T::BM;
+    f.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.xq + m0 * K), (short)0,
+                                             int(rows * K), kRsrcWord3);
+    const int64_t NB = (N + 15) / 16, rb0 = n0 / 16;
+    const int64_t blocks = NB - rb0 < T::BN / 16 ? NB - rb0 : T::BN / 16;
+    f.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(a.packed + 256 * rb0 * GP), (short)0,
+                                             int(blocks * GP * 1024), kRsrcWord3);
+    const int64_t cols = N - n0 < T::BN ? N - n0 : T::BN;
+    f.rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.q + n0 * G), (short)0, int(cols * G),
+                                             kRsrcWord3);
+  }
+  // activation staging: chunk c = tid + 256 i -> row c/16 = tid/16 + 16 i, 16-byte column tid%16
+  f.aoff = int((tid >> 4) * K) + 16 * (tid & 15);
+  f.astep = int(16 * K);
+  f.adst = (tid >> 4) * kAStride + 16 * (tid & 15);
+  // token scales of the tile's rows (LDS, read in the epilogue) and this lane's row scales
+  if (tid < T::BM) s_tok[tid] = a.tok_scale[m0 + tid < M ? m0 + tid : M - 1];
+  float rsv[J];
+  // weight columns of this lane: one per 32-wide N tile, read from the packed tiles
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int c = 32 * J * wave + 32 * j + l32;     // column inside the tile
+    f.boff[j] = (c >> 4) * GP * 1024 + 16 * (32 * h + (c & 15));
+    f.qoff[j] = c * G;
+    const int64_t n = n0 + c;
+    rsv[j] = a.row_scale[n < N ? n : N - 1];
+  }
+
+  v16i acc[MT][J];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
+
+  // The pair count is padded up to a multiple of 4 with leading zero-weight
+  // pairs, so that the loop below only exits after a whole ring turn.
+  // prologue: LDS buffers 0 and 1 <- pairs p0, p0+1; registers <- pair p0+2;
+  // weight ring <- pairs p0 .. p0+3.  Indices are clamped into [k0, k1) (valid
+  // memory; a clamped copy is either padding or never used).
+  const int plast = k1 - 1;
+  const int p0 = k0 - ((4 - (k1 - k0) % 4) % 4);
+  BStage<J> ring[4];
+  v4u anext[2][T::APieces];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load_b(ring[i], f, min(max(p0 + i, k0), plast), p0 + i >= k0);
+  load_a(anext[0], f, k0);
+  load_a(anext[1], f, min(max(p0 + 1, k0), plast));
+  store_a(sA, anext[0], f);
+  load_a(anext[0], f, min(max(p0 + 2, k0), plast));
+  store_a(sA + T::ABuf, anext[1], f);
+  load_a(anext[1], f, min(max(p0 + 3, k0), plast));
+  __syncthreads();
+
+  const int8_t *aread = sA + l32 * kAStride + 64 * h;
+  v4i af[2][MT], bf[2][J];
+  fetch_a(af[0], aread, 0);
+  fetch_b(bf[0], ring[0], 0);
+
+  int lb = 0;
+  for (int p = p0; p < k1; p += 4) {
+    pair_body<0, MT, J>(p, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+    pair_body<1, MT, J>(p + 1, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+    pair_body<2, MT, J>(p + 2, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+    pair_body<3, MT, J>(p + 3, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+  }
+
+  if (piece >= 0) {
+    // Split tile: publish this piece, and only the last piece to arrive goes on.
+    // Partials are written and read with device-scope atomic accesses (written
+    // through to, and read from, the point where all XCDs are coherent), so no
+    // whole-L2 fence is needed: the stores are waited for before the counter is
+    // bumped, and the reads are issued after the counter has answered.
+    // 16-byte pieces: piece (mt, j, r / 4) of thread tid at ((mt * J + j) * 4 + r / 4) * kThreads + tid,
+    // written and read with the system-coherent cache policy (sc1), like the
+    // device-scope atomic accesses, four elements per instruction
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + int64_t(slot - piece) * T::Ints, (short)0, int(sc.split * T::Ints * 4), kRsrcWord3);
+    const int mine = piece * T::Ints * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const v4i v = {acc[mt][j][4 * r4], acc[mt][j][4 * r4 + 1], acc[mt][j][4 * r4 + 2], acc[mt][j][4 * r4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128((v4u)v, rp, mine + 16 * (((mt * J + j) * 4 + r4) * kThreads + tid), 0,
+                                                 kCoherent);
+        }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every partial store has completed
+    __syncthreads();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(&a.counters[tile - sc.full], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = old == sc.split - 1;
+    }
+    __syncthreads();
+    if (!*s_last) return;
+    for (int o = 0; o < sc.split; ++o) {
+      if (o == piece) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(
+                rp, o * T::Ints * 4 + 16 * (((mt * J + j) * 4 + r4) * kThreads + tid), 0, kCoherent);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mt][j][4 * r4 + e] += (int)v[e];
+          }
+    }
+    if (tid == 0)  // leave the workspace as it was found
+      __hip_atomic_store(&a.counters[tile - sc.full], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  const bool whole = m0 + T::BM <= M && n0 + T::BN <= N;
+  if (whole && !a.acc_out && N % 8 == 0) {  // rows of y start on 16-byte boundaries
+    if (a.y_dtype == TL_F32) epilogue_lds<true>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
+    else epilogue_lds<false>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
+    return;
+  }
+  if (a.y_dtype == TL_F32) {
+    if (whole) epilogue<false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+    else epilogue<true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+  } else {
+    if (whole) epilogue<false, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+    else epilogue<true, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int64_t M, int64_t K,
     int64_t N, const uint32_t *__restrict__ packed, const int8_t *__restrict__ q,
@@ -323,15 +520,23 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   __shared__ __attribute__((aligned(16))) int8_t sA[3 * kABuf];
   __shared__ __attribute__((aligned(16))) float s_tok[kBM];
   __shared__ int s_last;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5;
-  const int G = int(K / kGroup);
-  const int GP = (G + 1) / 2;
+  const GemmArgs a{xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters};
+  const int GP = int((K / kGroup + 1) / 2);
 
   // which tile and which K range this workgroup computes
   const int g = blockIdx.x;
-  int tile, piece = 0, k0 = 0, k1 = GP;
+  if (g >= sc.full && sc.narrow) {
+    // sub-tile u of a left-over tile: rows 32 (u % 4), columns 128 (u / 4) of it
+    const int e = g - sc.full;
+    const int tile = sc.full + e / kNarrowPerTile, u = e % kNarrowPerTile;
+    constexpr int kRowCuts = Big::BM / Narrow::BM;
+    const int64_t m0 = int64_t(tile % sc.mb) * kBM + Narrow::BM * (u % kRowCuts);
+    const int64_t n0 = int64_t(tile / sc.mb) * kBN + Narrow::BN * (u / kRowCuts);
+    if (m0 >= M || n0 >= N) return;  // the whole sub-tile lies past the output
+    run_tile<Narrow::BM / 32, Narrow::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
+    return;
+  }
+  int tile, piece = -1, k0 = 0, k1 = GP;
   if (g < sc.full) {
     const int round = g / kSlots, u = g % kSlots;
     tile = (kSlots % kXcds == 0 && sc.full - round * kSlots >= kSlots)
@@ -346,141 +551,8 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   }
   const int64_t m0 = int64_t(tile % sc.mb) * kBM;
   const int64_t n0 = int64_t(tile / sc.mb) * kBN;
-
-  Frame f;
-  f.G = G;
-  {
-    const int64_t rows = M - m0 < kBM ? M - m0 : kBM;
-    f.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(xq + m0 * K), (short)0,
-                                             int(rows * K), kRsrcWord3);
-    const int64_t NB = (N + 15) / 16, rb0 = n0 / 16;
-    const int64_t blocks = NB - rb0 < kBN / 16 ? NB - rb0 : kBN / 16;
-    f.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(packed + 256 * rb0 * GP), (short)0,
-                                             int(blocks * GP * 1024), kRsrcWord3);
-    const int64_t cols = N - n0 < kBN ? N - n0 : kBN;
-    f.rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(q + n0 * G), (short)0, int(cols * G),
-                                             kRsrcWord3);
-  }
-  // activation staging: chunk c = tid + 256 i -> row c/16 = tid/16 + 16 i, 16-byte column tid%16
-  f.aoff = int((tid >> 4) * K) + 16 * (tid & 15);
-  f.astep = int(16 * K);
-  f.adst = (tid >> 4) * kAStride + 16 * (tid & 15);
-  // token scales of the tile's rows (LDS, read in the epilogue) and this lane's row scales
-  if (tid < kBM) s_tok[tid] = tok_scale[m0 + tid < M ? m0 + tid : M - 1];
-  float rsv[2];
-  // weight columns of this lane: one per 32-wide N tile, read from the packed tiles
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = 64 * wave + 32 * j + l32;         // column inside the tile
-    f.boff[j] = (c >> 4) * GP * 1024 + 16 * (32 * h + (c & 15));
-    f.qoff[j] = c * G;
-    const int64_t n = n0 + c;
-    rsv[j] = row_scale[n < N ? n : N - 1];
-  }
-
-  v16i acc[4][2];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
-
-  // The pair count is padded up to a multiple of 4 with leading zero-weight
-  // pairs, so that the loop below only exits after a whole ring turn.
-  // prologue: LDS buffers 0 and 1 <- pairs p0, p0+1; registers <- pair p0+2;
-  // weight ring <- pairs p0 .. p0+3.  Indices are clamped into [k0, k1) (valid
-  // memory; a clamped copy is either padding or never used).
-  const int plast = k1 - 1;
-  const int p0 = k0 - ((4 - (k1 - k0) % 4) % 4);
-  BStage ring[4];
-  v4u anext[2][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) load_b(ring[i], f, min(max(p0 + i, k0), plast), p0 + i >= k0);
-  load_a(anext[0], f, k0);
-  load_a(anext[1], f, min(max(p0 + 1, k0), plast));
-  store_a(sA, anext[0], f);
-  load_a(anext[0], f, min(max(p0 + 2, k0), plast));
-  store_a(sA + kABuf, anext[1], f);
-  load_a(anext[1], f, min(max(p0 + 3, k0), plast));
-  __syncthreads();
-
-  const int8_t *aread = sA + l32 * kAStride + 64 * h;
-  v4i af[2][4], bf[2][2];
-  fetch_a(af[0], aread, 0);
-  fetch_b(bf[0], ring[0], 0);
-
-  int lb = 0;
-  for (int p = p0; p < k1; p += 4) {
-    pair_body<0>(p, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-    pair_body<1>(p + 1, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-    pair_body<2>(p + 2, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-    pair_body<3>(p + 3, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-  }
-
-  if (g >= sc.full) {
-    // Split tile: publish this piece, and only the last piece to arrive goes on.
-    // Partials are written and read with device-scope atomic accesses (written
-    // through to, and read from, the point where all XCDs are coherent), so no
-    // whole-L2 fence is needed: the stores are waited for before the counter is
-    // bumped, and the reads are issued after the counter has answered.
-    const int slot = g - sc.full;                      // piece index among the left-over tiles
-    // 16-byte pieces: piece (mt, j, r / 4) of thread tid at ((mt * 2 + j) * 4 + r / 4) * kThreads + tid,
-    // written and read with the system-coherent cache policy (sc1), like the
-    // device-scope atomic accesses, four elements per instruction
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-        part + int64_t(slot - piece) * kTileInts, (short)0, int(sc.split * kTileInts * 4), kRsrcWord3);
-    const int mine = piece * kTileInts * 4;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const v4i v = {acc[mt][j][4 * r4], acc[mt][j][4 * r4 + 1], acc[mt][j][4 * r4 + 2], acc[mt][j][4 * r4 + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128((v4u)v, rp, mine + 16 * (((mt * 2 + j) * 4 + r4) * kThreads + tid), 0,
-                                                 kCoherent);
-        }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every partial store has completed
-    __syncthreads();
-    if (tid == 0) {
-      const int old = __hip_atomic_fetch_add(&counters[tile - sc.full], 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      s_last = old == sc.split - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    for (int o = 0; o < sc.split; ++o) {
-      if (o == piece) continue;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const v4u v = __builtin_amdgcn_raw_buffer_load_b128(
-                rp, o * kTileInts * 4 + 16 * (((mt * 2 + j) * 4 + r4) * kThreads + tid), 0, kCoherent);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[mt][j][4 * r4 + e] += (int)v[e];
-          }
-    }
-    if (tid == 0)  // leave the workspace as it was found
-      __hip_atomic_store(&counters[tile - sc.full], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  const bool whole = m0 + kBM <= M && n0 + kBN <= N;
-  if (whole && !acc_out && N % 8 == 0) {  // rows of y start on 16-byte boundaries
-    if (y_dtype == TL_F32) epilogue_lds<true>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, y, sA);
-    else epilogue_lds<false>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, y, sA);
-    return;
-  }
-  if (y_dtype == TL_F32) {
-    if (whole) epilogue<false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
-    else epilogue<true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
-  } else {
-    if (whole) epilogue<false, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
-    else epilogue<true, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, y, acc_out);
-  }
+  run_tile<Big::BM / 32, Big::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece,
+                                        g - sc.full);
 }
 
 // Workspace layout, the same for every shape so that one workspace serves calls
@@ -510,7 +582,8 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
                      M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
-  set_last_kernel(s.split > 1 ? "gemm_i8_mfma32_128x256_splitk" : "gemm_i8_mfma32_128x256");
+  set_last_kernel(s.narrow ? "gemm_i8_mfma32_128x256_narrowtail"
+                           : s.split > 1 ? "gemm_i8_mfma32_128x256_splitk" : "gemm_i8_mfma32_128x256");
   return hipGetLastError();
 }
 

@@ -128,10 +128,12 @@ def test_gemm_rejections():
     assert L.tl_gemm_int8_rescale(*args(acc=ODD, y=ctypes.c_void_p(0xA0000000))) == 3
     assert L.tl_gemm_int8_rescale(*args(y=FAKE)) == 8
     assert L.tl_gemm_int8_rescale(*args(M=0)) == 0
-    # 512 x 34816 leaves 32 of 544 tiles for a last round: they are split along K
-    need = L.tl_gemm_workspace_size(512, 5120, 34816)
+    # 512 x 40960 leaves 128 of 640 tiles for a last round: they are split along K;
+    # 512 x 34816 leaves 32 of 544, cut into sub-tiles that need no workspace
+    need = L.tl_gemm_workspace_size(512, 5120, 40960)
     assert need > 0 and L.tl_gemm_workspace_size(512, 5120, 32768) == 0
-    big = lambda ws, wb: (FAKE, FAKE2, 512, 5120, 34816, FAKE3, FAKE4, FAKE5, ctypes.c_void_p(0xA0000000),
+    assert L.tl_gemm_workspace_size(512, 5120, 34816) == 0
+    big = lambda ws, wb: (FAKE, FAKE2, 512, 5120, 40960, FAKE3, FAKE4, FAKE5, ctypes.c_void_p(0xA0000000),
                           1, None, ws, wb, None)
     assert L.tl_gemm_int8_rescale(*big(None, 0)) == 7
     assert L.tl_gemm_int8_rescale(*big(ctypes.c_void_p(0xC0000000), need - 1)) == 7

@@ -307,6 +307,21 @@ def test_gemm_ragged(tl, M, K, N):
     _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "ragged")
 
 
+@pytest.mark.parametrize("M,K,N", [(300, 256, 22940), (130, 384, 4000)])
+def test_gemm_narrow_tail(tl, M, K, N):
+    """A short last round cut into 32 x 128 sub-tiles, some of them partly or wholly
+    past M and N (300 rows = 2 whole M-blocks + 44 rows; a ragged last strip)."""
+    d = dev()
+    rng = np.random.default_rng(M + K + N)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.exp(rng.standard_normal(M)).astype(np.float32)
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "narrow tail")
+    assert tl.last_kernel_name().endswith("narrowtail")
+
+
 def test_gemm_workspace_reused_across_shapes(tl):
     """One workspace, K-split GEMMs of different shapes in turn (64 and 128 split
     tiles): the counters of one shape never overlap the partials of another, and
