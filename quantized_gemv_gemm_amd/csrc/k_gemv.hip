@@ -37,6 +37,9 @@
 // Rows past N and token slots past b read clamped, valid addresses (no divergent
 // branches around loads) and their results are never stored.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "tl_device.h"
 
@@ -715,9 +718,9 @@ constexpr int kPmaxLds = 5;   // pairs per wave, limbs in LDS
 constexpr int kPmaxReg = 3;   // pairs per wave, A fragments in registers
 constexpr int kMaxWaves = 16;
 
-// Row blocks per workgroup: the smallest of 1, 2, 4 whose workgroups all fit on
-// the chip at once (one round), given how many fit per compute unit by LDS and
-// by waves; 4 when none does.
+// Row blocks per workgroup of the int8-activation variant: the smallest of 1, 2, 4
+// whose workgroups all fit on the chip at once (one round), given how many fit per
+// compute unit by LDS and by waves; 4 when none does.
 constexpr int kCUs = 256;
 constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kWavesPerCU = 32;
@@ -730,6 +733,10 @@ int fit_rb(int64_t N, int64_t chunks, size_t lds_fixed, size_t lds_per_rb, int w
   }
   return 4;
 }
+
+// workgroups of a stream-kernel variant resident per compute unit (defined after
+// the launch helpers); 0 when the runtime cannot tell
+int stream_resident(bool alds, int rb, int64_t b, int pmax, int waves, size_t lds);
 
 GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   // more than 16 tokens: one grid row per chunk of 16, each shaped like b = 16
@@ -752,22 +759,45 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
       }
     }
   };
+  // Row blocks per workgroup, 1..4: the smallest whose workgroups are all resident
+  // at once (one round), else the one with the lowest rounds x (3 + RB).  A
+  // workgroup costs about 3 row blocks' worth of weight streaming for its fixed
+  // part (limbs, scales, reduction) plus one per row block: the fit to measured qkv
+  // and gate_up launches at b = 1..16 (RB = 3 beat 4 by 7-14 % at b = 8 and 16).
+  // Residency: the runtime's occupancy figure for the variant (its registers and
+  // LDS), cached per variant.
+  auto choose_rb = [&](bool alds, int pmax0, size_t lds_limbs) {
+    int best = 4;
+    int64_t best_cost = INT64_MAX;
+    for (int rb = 1; rb <= 4; ++rb) {
+      shape(alds, rb, pmax0);
+      const size_t lds = lds_limbs + scale_lds_bytes(16 * rb, int(G)) +
+                         size_t(p.waves > 1 ? p.waves - 1 : 1) * rb * nt * 256;
+      int64_t per_cu = stream_resident(alds, rb, b, p.pmax, p.waves, lds);
+      if (per_cu <= 0) {  // no answer from the runtime: bound by LDS and the register budget
+        const int wave_cap = stream_heavy(alds, rb, p.pmax, lp) ? 8 : 16;
+        per_cu = std::max<int64_t>(1, std::min<int64_t>(int64_t(kLdsPerCU / lds), wave_cap / p.waves));
+      }
+      const int64_t wgs = (N + 16 * rb - 1) / (16 * rb) * chunks;
+      const int64_t rounds = (wgs + per_cu * kCUs - 1) / (per_cu * kCUs);
+      if (rounds == 1) return rb;
+      if (rounds * (3 + rb) < best_cost) best_cost = rounds * (3 + rb), best = rb;
+    }
+    return best;
+  };
   if (limb_bytes <= kLdsLimbBudget && GP <= 8 * kPmaxLds) {
     // limbs in LDS.  Small batches: few waves with several pairs each, so that
     // pairs are computed while later ones arrive; b > 4: up to four row blocks
     // share one copy of the limbs.
     p.kind = 0;
     p.lds_limb_bytes = int(limb_bytes);
-    shape(true, 1, b <= 4 ? 5 : 3);
-    p.rb = fit_rb(N, chunks, size_t(limb_bytes), scale_lds_bytes(16, int(G)) + size_t(p.waves) * nt * 256,
-                  p.waves);
-    if (b <= 4) p.rb = std::min(p.rb, 2);
-    shape(true, p.rb, p.pmax);
+    p.rb = choose_rb(true, b <= 4 ? 5 : 3, size_t(limb_bytes));
+    shape(true, p.rb, b <= 4 ? 5 : 3);
   } else if (GP <= 8 * kPmaxReg) {
     // limbs from L2 into registers, all pairs at once
     p.kind = 1;
     p.lds_limb_bytes = 0;
-    p.rb = (N + 63) / 64 >= 128 ? 4 : (N + 31) / 32 >= 128 ? 2 : 1;  // A fragments serve RB tiles
+    p.rb = choose_rb(false, 2, 0);
     shape(false, p.rb, 2);
   } else {
     p.kind = 2;
@@ -779,10 +809,11 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   }
   p.lds_bytes = size_t(p.lds_limb_bytes) + scale_lds_bytes(16 * p.rb, int(G)) +
                 size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * nt * 64 * sizeof(float);
-  static const char *names[3][3] = {{"gemv_stream_lds_rb1", "gemv_stream_lds_rb2", "gemv_stream_lds_rb4"},
-                                    {"gemv_stream_reg_rb1", "gemv_stream_reg_rb2", "gemv_stream_reg_rb4"},
-                                    {"gemv_ring_rb1", "gemv_ring_rb2", "gemv_ring_rb2"}};
-  p.name = names[p.kind][p.rb == 4 ? 2 : p.rb - 1];
+  static const char *names[3][4] = {
+      {"gemv_stream_lds_rb1", "gemv_stream_lds_rb2", "gemv_stream_lds_rb3", "gemv_stream_lds_rb4"},
+      {"gemv_stream_reg_rb1", "gemv_stream_reg_rb2", "gemv_stream_reg_rb3", "gemv_stream_reg_rb4"},
+      {"gemv_ring_rb1", "gemv_ring_rb2", "gemv_ring_rb2", "gemv_ring_rb2"}};
+  p.name = names[p.kind][p.rb - 1];
   p.chunks = int(chunks);
   return p;
 }
@@ -795,10 +826,17 @@ struct GemvArgs {
   void *y;
   int y_dtype;
   hipStream_t stream;
+  int *resident = nullptr;  // set: report workgroups per CU for the variant instead of launching
 };
 
 template <int RB, int NT, int PMAX, bool LP, bool ALDS>
 void launch_stream_t(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
+  if (a.resident) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(a.resident, gemv_stream_kernel<RB, NT, PMAX, LP, ALDS>,
+                                                     64 * p.waves, p.lds_bytes) != hipSuccess)
+      *a.resident = 0;
+    return;
+  }
   hipLaunchKernelGGL((gemv_stream_kernel<RB, NT, PMAX, LP, ALDS>), grid, dim3(64 * p.waves), p.lds_bytes,
                      a.stream, a.w->xhi, a.w->sigma, int(a.b), a.K, a.w->Kp, a.N, a.packed, a.scales, a.y,
                      a.y_dtype, p.lds_limb_bytes);
@@ -835,7 +873,8 @@ void launch_stream_n(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
 
 template <bool ALDS>
 void launch_stream(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
-  if (p.rb == 4) launch_stream_n<4, ALDS>(p, grid, a);
+  if (p.rb == 3) launch_stream_n<3, ALDS>(p, grid, a);
+  else if (p.rb == 4) launch_stream_n<4, ALDS>(p, grid, a);
   else if (p.rb == 2) launch_stream_n<2, ALDS>(p, grid, a);
   else launch_stream_n<1, ALDS>(p, grid, a);
 }
@@ -939,6 +978,34 @@ size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
   // two int8 limb planes [b, K + 16] and the per-token scales
   return align256(size_t(limb_region_bytes(b, K))) + align256(size_t(kGemvMaxTokens) * sizeof(float));
 }
+
+namespace {
+int stream_resident(bool alds, int rb, int64_t b, int pmax, int waves, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<bool, int, int64_t, int, int, size_t>, int> cache;
+  const auto key = std::make_tuple(alds, rb, std::min<int64_t>(b, kTokChunk), pmax, waves, lds);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  GemvPlan p{};
+  p.rb = rb;
+  p.pmax = pmax;
+  p.waves = waves;
+  p.lds_bytes = lds;
+  int n = 0;
+  GemvArgs a{};
+  a.b = b;
+  a.resident = &n;
+  if (alds) launch_stream<true>(p, dim3(1), a);
+  else launch_stream<false>(p, dim3(1), a);
+  (void)hipGetLastError();  // a failed query leaves no error behind
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = n;
+  return n;
+}
+}  // namespace
 
 hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
                                hipStream_t stream) {
