@@ -323,6 +323,43 @@ def main():
     prep_ms = {b: [run_time(lambda: tl.gemv_prepare_x(x_dec[b], ws_dec[b]))] for b in DECODE_BS}
     quant_ms = {k: [run_time(lambda: tl.quant_act_int8_x(P["x"], xq=P["xq"], tok_scale=P["sx"]))]
                 for k, P in pre.items()}
+    # Launch-cost fit of the GEMV weight stream, t = F + bytes / BW, over the three
+    # layer shapes (qkv, down, gate_up: 14 to 48 MB) at b = 1 and 16, each the mean of
+    # DEC_LAYERS back-to-back launches over rotating weight copies behind a spin:
+    # F is the fixed per-launch cost, BW the rate at which the kernel streams.
+    fit = {}
+    fit_shapes = (("qkv", qkv, 5120, 10240), ("down", pre["down"]["copies"], 17408, 5120),
+                  ("gate_up", pre["gate_up"]["copies"], 5120, 34816))
+    for b in (1, 16):
+        pts = []
+        for name, copies, K, N in fit_shapes:
+            xr = tl.hadamard_blk(bf16(synth.activations(0, 2, 7, b, K)))
+            ws = torch.empty((tl.gemv_workspace_size(b, K, N),), dtype=torch.uint8, device=dev)
+            yb = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
+            tl.gemv_prepare(xr, ws)
+            k = [0]
+
+            def one():
+                packed, scales = copies[k[0] % len(copies)][:2]
+                k[0] += 1
+                tl.gemv_prepared(ws, b, K, packed, scales, yb)
+            t_us = run_time(one, n=DEC_LAYERS * 4) * 1e3
+            pts.append((gemv_bytes(b, K, N), t_us, name, tl.last_kernel_name()))
+        xs = np.array([p[0] for p in pts], dtype=np.float64)
+        ts = np.array([p[1] for p in pts], dtype=np.float64)
+        slope, icpt = np.polyfit(xs, ts, 1)          # µs per byte, µs
+        bw = 1e-3 / slope                            # GB/s
+        fit[f"b{b}"] = {"F_us": round(float(icpt), 2), "BW_GBps": round(float(bw), 1),
+                        "BW_frac": round(float(bw) / HBM_PEAK_GBS, 4),
+                        "points": [{"shape": n, "bytes": int(x), "us": round(t, 2), "kernel": kn}
+                                   for x, t, n, kn in pts]}
+    # the rotation alone (tl_hadamard_blk: bf16 in, f32 out), at the decode and prefill sizes
+    rot_only = {}
+    for label, xs in (("decode_b16_k5120", x_dec[16]), ("prefill_m512_k17408", pre["down"]["x"])):
+        xr_o = torch.empty(xs.shape, dtype=torch.float32, device=dev)
+        t_ms = run_time(lambda: tl.hadamard_blk(xs, out=xr_o))
+        nb = xs.numel() * 6
+        rot_only[label] = {"us": round(t_ms * 1e3, 2), "GBps": round(nb / (t_ms * 1e-3) / 1e9, 1)}
     # split-block rotation stages of a TP=2 shard boundary (down_proj's block 8):
     # the half stage on a column slice of the raw input, the join into the rank's columns
     split_us = {}
@@ -370,6 +407,7 @@ def main():
             pre_out[k]["traffic_bytes"] = traffic["gemm"][k]["traffic_bytes"]
         gemm_traffic = round(float(np.mean([traffic["gemm"][k]["traffic_bytes"] for k in pre_out])))
 
+    pre_k = {k: P["K"] for k, P in pre.items()}
     stack = None
     if not args.no_stack:
         del qkv, gate_up, down, pre
@@ -401,6 +439,14 @@ def main():
                    "decode_b": list(DECODE_BS), "prefill_tokens": PREFILL_M,
                    "rotating_weight_bytes": ROTATE_BYTES},
         "decode_gemv_by_b": by_b,
+        "gemv_launch_fit": fit,
+        "rotation_only": rot_only,
+        "input_kernels_GBps": {
+            "decode_rotate_prep": {str(b): round((2 * b * Kq + 2 * b * Kq + 4 * b) / (float(np.mean(prep_ms[b])) * 1e-3) / 1e9, 1)
+                                   for b in DECODE_BS},
+            "prefill_rotate_quant_m512": {k: round((3 * PREFILL_M * pre_k[k] + 4 * PREFILL_M) /
+                                                   (float(np.mean(v)) * 1e-3) / 1e9, 1)
+                                          for k, v in quant_ms.items()}},
         "input_kernels_us": {
             "decode_rotate_prep": {str(b): round(float(np.mean(prep_ms[b])) * 1e3, 2) for b in DECODE_BS},
             "prefill_rotate_quant_m512": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in quant_ms.items()},
