@@ -38,6 +38,8 @@
 //    the workspace and bumps the tile's counter, and the piece that arrives last
 //    adds the others and runs the epilogue (integer sums: exact and order
 //    independent).
+// The left-over work is dealt out XCD by XCD (workgroup i runs on XCD i % 8), so
+// that the pieces or sub-tiles of one weight strip share an L2.
 // No workgroup ever waits for another.
 #include <algorithm>
 
@@ -90,8 +92,8 @@ struct Schedule {
   int full;       // tiles computed whole, in rounds of kSlots (the rest are split or cut)
   int split;      // pieces per left-over tile along K (1: nothing is split)
   int narrow;     // 1: the left-over tiles are cut into kNarrowPerTile sub-tiles
-  int64_t left() const { return split > 1 || narrow ? tiles - full : 0; }
-  int64_t grid() const { return full + left() * (narrow ? kNarrowPerTile : split); }
+  __host__ __device__ int64_t left() const { return split > 1 || narrow ? tiles - full : 0; }
+  __host__ __device__ int64_t grid() const { return full + left() * (narrow ? kNarrowPerTile : split); }
 };
 
 __device__ __forceinline__ uint32_t perm_table(int qv) {
@@ -511,6 +513,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
   }
 }
 
+// Work item of left-over workgroup e of `total`: workgroup e runs on XCD e % kXcds,
+// so the items are dealt out XCD by XCD, each XCD taking a contiguous run (the
+// pieces or sub-tiles of neighbouring tiles share weight strips and so its L2).
+__device__ __forceinline__ int xcd_item(int e, int total) {
+  if (total % kXcds) return e;
+  return (total / kXcds) * (e % kXcds) + e / kXcds;
+}
+
 __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int64_t M, int64_t K,
     int64_t N, const uint32_t *__restrict__ packed, const int8_t *__restrict__ q,
@@ -527,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   const int g = blockIdx.x;
   if (g >= sc.full && sc.narrow) {
     // sub-tile u of a left-over tile: rows 32 (u % 4), columns 128 (u / 4) of it
-    const int e = g - sc.full;
+    const int e = xcd_item(g - sc.full, int(sc.grid() - sc.full));
     const int tile = sc.full + e / kNarrowPerTile, u = e % kNarrowPerTile;
     constexpr int kRowCuts = Big::BM / Narrow::BM;
     const int64_t m0 = int64_t(tile % sc.mb) * kBM + Narrow::BM * (u % kRowCuts);
@@ -536,23 +546,22 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     run_tile<Narrow::BM / 32, Narrow::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
     return;
   }
-  int tile, piece = -1, k0 = 0, k1 = GP;
+  int tile, piece = -1, slot = 0, k0 = 0, k1 = GP;
   if (g < sc.full) {
     const int round = g / kSlots, u = g % kSlots;
     tile = (kSlots % kXcds == 0 && sc.full - round * kSlots >= kSlots)
                ? round * kSlots + (kSlots / kXcds) * (u % kXcds) + u / kXcds
                : g;
   } else {
-    const int e = g - sc.full;
-    tile = sc.full + e / sc.split;
-    piece = e % sc.split;
+    slot = xcd_item(g - sc.full, int(sc.grid() - sc.full));
+    tile = sc.full + slot / sc.split;
+    piece = slot % sc.split;
     k0 = int(int64_t(GP) * piece / sc.split);
     k1 = int(int64_t(GP) * (piece + 1) / sc.split);
   }
   const int64_t m0 = int64_t(tile % sc.mb) * kBM;
   const int64_t n0 = int64_t(tile / sc.mb) * kBN;
-  run_tile<Big::BM / 32, Big::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece,
-                                        g - sc.full);
+  run_tile<Big::BM / 32, Big::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
 }
 
 // Workspace layout, the same for every shape so that one workspace serves calls
