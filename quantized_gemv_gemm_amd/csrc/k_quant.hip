@@ -3,9 +3,9 @@
 // Method: qiita.com/nakanokensetsu/items/ecc183fae033565af7cb, "4. 効いた高速化":
 // activations are quantised to int8 per token after the Hadamard rotation (which
 // evens out outliers).  Symmetric absmax: sx = fl32(amax / 127),
-// xq = clamp(RNE(fl32(x / sx)), -127, 127).  Both quotients are formed in
-// binary64 and rounded to binary32 once, which equals the correctly rounded
-// binary32 division.
+// xq = clamp(RNE(fl32(x / sx)), -127, 127).  sx is the binary64 quotient rounded
+// once to binary32; the codes use the IEEE binary32 division (both correctly
+// rounded).
 //
 // One workgroup per token: a max-reduction pass, then a quantisation pass that
 // re-reads the row (L2-resident) and writes 16 codes per 16-byte store.
@@ -17,17 +17,12 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint32_t quant4(float4 v, double sxd, bool live) {
+__device__ __forceinline__ uint32_t quant4(float4 v, float sx, bool live) {
   const float f[4] = {v.x, v.y, v.z, v.w};
   uint32_t out = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int qi = 0;
-    if (live) {
-      const float quo = (float)((double)f[i] / sxd);
-      qi = (int)rintf(quo);
-      qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-    }
+    const int qi = live ? quant_code(f[i], sx) : 0;
     out |= (uint32_t)(qi & 0xFF) << (8 * i);
   }
   return out;
@@ -48,15 +43,14 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const float *__rest
   const float sx = (float)((double)amax / 127.0);
   if (threadIdx.x == 0) tok_scale[t] = sx;
   const bool live = sx > 0.0f;
-  const double sxd = (double)sx;
   int8_t *orow = xq + t * K;
   for (int64_t i = 16 * threadIdx.x; i < K; i += 16 * kThreads) {
     const float4 *src = reinterpret_cast<const float4 *>(row + i);
     uint4 o;
-    o.x = quant4(src[0], sxd, live);
-    o.y = quant4(src[1], sxd, live);
-    o.z = quant4(src[2], sxd, live);
-    o.w = quant4(src[3], sxd, live);
+    o.x = quant4(src[0], sx, live);
+    o.y = quant4(src[1], sx, live);
+    o.z = quant4(src[2], sx, live);
+    o.w = quant4(src[3], sx, live);
     *reinterpret_cast<uint4 *>(orow + i) = o;
   }
 }

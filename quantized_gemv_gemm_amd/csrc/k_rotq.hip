@@ -7,12 +7,17 @@
 // Both kernels produce exactly what the unfused pair produces: the rotation is the
 // same wave routine (exact in binary64, rounded once to f32), the token maximum is
 // over those f32 values, and each element is then converted with the same f32 /
-// binary64 expressions as the GEMV prep and the quantisation kernels.
+// binary64 expressions as the GEMV prep and the quantisation kernels (quant_code).
 //
-// One workgroup per token, W = min(K/1024, 16) waves; wave w rotates blocks
-// w, w + W, ... into registers (at most BPW blocks), the workgroup reduces |x|max,
-// and every lane converts and stores its own elements (lane + 64 j of each block:
-// 64 consecutive bytes per wave store).
+// One workgroup per token of W waves; wave w rotates blocks w, w + W, ... into
+// registers (at most BPW blocks, W = ceil(blocks / BPW) <= 16, BPW chosen by
+// fuse_shape), the workgroup reduces |x|max, and every lane converts and stores
+// its own elements (lane + 64 j of each block: 64 consecutive bytes per wave store).
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "rotate_dev.h"
 
 namespace tl {
@@ -27,12 +32,25 @@ __device__ __forceinline__ float rotate_token(const uint16_t *__restrict__ xrow,
                                               double *lds, int wave, int W, int lane,
                                               float (&r)[BPW][kRotEPT]) {
   float m = 0.0f;
+  // every block's inputs are requested before the first rotation starts (up to
+  // three blocks per wave; beyond that the raw inputs would not fit the registers)
+  constexpr int kPre = BPW <= 3 ? BPW : 1;
+  RotRaw raw[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int blk = wave + i * W;
+    if (blk < nblk)
+      rotate_load(xrow + int64_t(blk) * kHBlock, signs ? signs + int64_t(blk) * kHBlock : nullptr, lane,
+                  raw[i]);
+  }
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
     const int blk = wave + i * W;
     if (blk < nblk) {
-      rotate_block_wave(xrow + int64_t(blk) * kHBlock, signs ? signs + int64_t(blk) * kHBlock : nullptr,
-                        lds, lane, r[i]);
+      if (i >= kPre)
+        rotate_load(xrow + int64_t(blk) * kHBlock, signs ? signs + int64_t(blk) * kHBlock : nullptr, lane,
+                    raw[0]);
+      rotate_block_raw(raw[i < kPre ? i : 0], signs != nullptr, lds, lane, r[i]);
 #pragma unroll
       for (int j = 0; j < kRotEPT; ++j) m = fmaxf(m, fabsf(r[i][j]));
     }
@@ -103,7 +121,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void quant_x_kernel(
   const float sx = (float)((double)amax / 127.0);
   if (threadIdx.x == 0) tok_scale[t] = sx;
   const bool live = sx > 0.0f;
-  const double sxd = (double)sx;
   int8_t *orow = xq + t * K;
 #pragma unroll
   for (int i = 0; i < BPW; ++i) {
@@ -111,11 +128,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void quant_x_kernel(
     if (blk < nblk) {
 #pragma unroll
       for (int j = 0; j < kRotEPT; ++j) {
-        int qi = 0;
-        if (live) {
-          qi = (int)rintf((float)((double)r[i][j] / sxd));
-          qi = qi > 127 ? 127 : (qi < -127 ? -127 : qi);
-        }
+        const int qi = live ? quant_code(r[i][j], sx) : 0;
         orow[int64_t(blk) * kHBlock + lane + 64 * j] = (int8_t)qi;
       }
     }
@@ -127,13 +140,58 @@ struct FuseShape {
   size_t lds;
 };
 
-FuseShape fuse_shape(int64_t K) {
+template <int BPW>
+const void *fuse_kernel(bool quant) {
+  return quant ? reinterpret_cast<const void *>(quant_x_kernel<BPW>)
+               : reinterpret_cast<const void *>(gemv_prep_x_kernel<BPW>);
+}
+
+// workgroups of a fused-input variant resident per compute unit (0: unknown)
+int fuse_resident(bool quant, int bpw, int waves) {
+  static std::mutex mu;
+  static std::map<std::tuple<bool, int, int>, int> cache;
+  const auto key = std::make_tuple(quant, bpw, waves);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  const void *fn = bpw == 1 ? fuse_kernel<1>(quant) : bpw == 2 ? fuse_kernel<2>(quant)
+                 : bpw == 3 ? fuse_kernel<3>(quant) : fuse_kernel<4>(quant);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, 64 * waves,
+                                                   size_t(waves) * kRotLds * sizeof(double)) != hipSuccess)
+    n = 0;
+  (void)hipGetLastError();
+  std::lock_guard<std::mutex> lock(mu);
+  cache[key] = n;
+  return n;
+}
+
+// Blocks per wave (and so waves per workgroup, one workgroup per token): the
+// fewest rounds x blocks per wave, where a round is as many tokens as the chip
+// holds at once (residency from the runtime's occupancy figure, else by LDS).
+// Few tokens (decode): one round whatever the shape, so one block per wave.
+// 512 tokens of K = 17408 (17 blocks): 6 waves x 3 blocks, two workgroups per CU,
+// rather than 16 waves x 2 blocks with one (LDS) and a wave left doing two blocks.
+FuseShape fuse_shape(int64_t K, int64_t T, bool quant) {
   const int nblk = int(K / kHBlock);
-  FuseShape s;
-  s.waves = nblk < kMaxWaves ? nblk : kMaxWaves;
-  s.bpw = (nblk + s.waves - 1) / s.waves;
-  s.lds = size_t(s.waves) * kRotLds * sizeof(double);
-  return s;
+  FuseShape best{};
+  int64_t best_cost = INT64_MAX;
+  for (int bpw = 1; bpw <= 4; ++bpw) {
+    const int waves = (nblk + bpw - 1) / bpw;
+    if (waves > kMaxWaves) continue;
+    if (bpw == 4 && nblk <= 3 * kMaxWaves) continue;  // four blocks per wave spill: only when needed
+    const size_t lds = size_t(waves) * kRotLds * sizeof(double);
+    int64_t per_cu = fuse_resident(quant, bpw, waves);
+    if (per_cu <= 0) per_cu = std::max<int64_t>(1, int64_t(160 * 1024 / lds));
+    const int64_t rounds = (T + 256 * per_cu - 1) / (256 * per_cu);
+    if (rounds * bpw < best_cost) {
+      best_cost = rounds * bpw;
+      best = FuseShape{waves, bpw, lds};
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -142,7 +200,7 @@ bool fused_input_supported(int64_t K) { return K > 0 && K % kHBlock == 0 && K <=
 
 hipError_t launch_gemv_prepare_x(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
                                  int8_t *xhi, int64_t Kp, float *sigma, hipStream_t stream) {
-  const FuseShape s = fuse_shape(K);
+  const FuseShape s = fuse_shape(K, b, false);
   const dim3 grid{unsigned(b)}, blk{unsigned(64 * s.waves)};
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   switch (s.bpw) {
@@ -158,7 +216,7 @@ hipError_t launch_gemv_prepare_x(const uint16_t *x, int64_t b, int64_t K, const 
 hipError_t launch_quant_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *signs, int8_t *xq,
                           float *tok_scale, hipStream_t stream) {
   if (T > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const FuseShape s = fuse_shape(K);
+  const FuseShape s = fuse_shape(K, T, true);
   const dim3 grid{unsigned(T)}, blk{unsigned(64 * s.waves)};
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
   switch (s.bpw) {

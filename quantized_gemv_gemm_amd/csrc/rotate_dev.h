@@ -44,26 +44,36 @@ __device__ __forceinline__ void rot_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Rotates the 1024 bf16 values at xblk (signs: NULL or the block's 1024 signs).
-// On return out[j] = fl32(rotation[lane + 64 j]).  lds: kRotLds doubles owned by
-// the calling wavefront.
-__device__ __forceinline__ void rotate_block_wave(const uint16_t *__restrict__ xblk,
-                                                  const int8_t *__restrict__ sblk, double *lds,
-                                                  int lane, float (&out)[kRotEPT]) {
+// The lane's raw inputs of one block: its 16 consecutive bf16 values and signs.
+struct RotRaw {
+  uint4 a, b;  // bf16 elements 16 lane .. 16 lane + 15
+  uint4 s;     // their signs (when a sign table is given)
+};
+
+__device__ __forceinline__ void rotate_load(const uint16_t *__restrict__ xblk,
+                                            const int8_t *__restrict__ sblk, int lane, RotRaw &r) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(xblk + kRotEPT * lane);
+  r.a = src[0];
+  r.b = src[1];
+  if (sblk) r.s = *reinterpret_cast<const uint4 *>(sblk + kRotEPT * lane);
+}
+
+// Rotates one block from the lane's raw inputs (loaded by rotate_load; signs used
+// when `signed_in`).  On return out[j] = fl32(rotation[lane + 64 j]).  lds: kRotLds
+// doubles owned by the calling wavefront.
+__device__ __forceinline__ void rotate_block_raw(const RotRaw &r, bool signed_in, double *lds, int lane,
+                                                 float (&out)[kRotEPT]) {
   // phase A: lane owns elements 16*lane + j
   double v[kRotEPT];
   {
-    const uint4 *src = reinterpret_cast<const uint4 *>(xblk + kRotEPT * lane);
-    const uint4 a = src[0], b = src[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       v[2 * j] = (double)bf16_bits_to_float(w[j] & 0xFFFFu);
       v[2 * j + 1] = (double)bf16_bits_to_float(w[j] >> 16);
     }
-    if (sblk) {
-      const uint4 s = *reinterpret_cast<const uint4 *>(sblk + kRotEPT * lane);
-      const uint32_t sw[4] = {s.x, s.y, s.z, s.w};
+    if (signed_in) {
+      const uint32_t sw[4] = {r.s.x, r.s.y, r.s.z, r.s.w};
 #pragma unroll
       for (int j = 0; j < kRotEPT; ++j) {
         const int8_t d = (int8_t)((sw[j >> 2] >> (8 * (j & 3))) & 0xFF);
@@ -99,6 +109,15 @@ __device__ __forceinline__ void rotate_block_wave(const uint16_t *__restrict__ x
 #pragma unroll
   for (int j = 0; j < kRotEPT; ++j) out[j] = (float)(v[j] * 0.03125);
   rot_wave_sync();  // the next block may overwrite lds
+}
+
+// Rotates the 1024 bf16 values at xblk (signs: NULL or the block's 1024 signs).
+__device__ __forceinline__ void rotate_block_wave(const uint16_t *__restrict__ xblk,
+                                                  const int8_t *__restrict__ sblk, double *lds,
+                                                  int lane, float (&out)[kRotEPT]) {
+  RotRaw r;
+  rotate_load(xblk, sblk, lane, r);
+  rotate_block_raw(r, sblk != nullptr, lds, lane, out);
 }
 
 }  // namespace tl

@@ -25,6 +25,14 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// int8 code of x for the per-token scale sx > 0: clamp(RNE(fl32(x / sx)), -127, 127).
+// The quotient is the IEEE binary32 division (correctly rounded; no fast-math),
+// which equals rounding the binary64 quotient once to binary32 (53 >= 2 * 24 + 2).
+__device__ __forceinline__ int quant_code(float x, float sx) {
+  const int q = (int)rintf(x / sx);
+  return q > 127 ? 127 : (q < -127 ? -127 : q);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
