@@ -69,6 +69,9 @@ def parse():
     p.add_argument("--stack-steps", type=int, default=5)
     p.add_argument("--bsweep", action="store_true",
                    help="token-count sweep of the two layer paths (GEMV vs int8 GEMM) instead of the bench")
+    p.add_argument("--library-reference", action="store_true",
+                   help="time torch._int_mm (the vendor int8 GEMM the pages' prefill calls) at the prefill "
+                        "shapes, with int8 weights already expanded, beside this library's GEMM")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -190,6 +193,9 @@ def main():
 
     if args.bsweep:
         bsweep(tl, torch, dev, log)
+        return
+    if args.library_reference:
+        library_reference(tl, torch, dev)
         return
 
     # ---------------- weights (packed once, cloned into rotating copies) ----------------
@@ -463,6 +469,50 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def library_reference(tl, torch, dev, n=20):
+    """torch._int_mm (int8 x int8 -> int32 on the vendor GEMM library; the call [P1] §4
+    makes after expanding the weights to int8 each step) against tl_gemm_int8_rescale
+    (2-bit weights expanded in registers, rescale fused) at the same shapes.  Weights
+    rotate over copies beyond the Infinity Cache; n launches behind a device spin
+    between two HIP events.  _int_mm gets its int8 weight matrix ready-made (its
+    expansion is not timed) and writes int32; ours writes bf16 after the rescale."""
+    import synth
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        torch.cuda._sleep(3_000_000)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+    for (M, K, N) in ((512, 5120, 34816), (512, 17408, 5120), (2048, 5120, 34816)):
+        L = synth.LayerInputs(0, 3, 1, K, N)
+        codes = L.codes_torch(dev)
+        scales = torch.from_numpy(L.scales()).to(dev)
+        packed, q, rs = tl.pack_weights(codes, scales)
+        del codes
+        R = max(2, min(12, math.ceil(ROTATE_BYTES / (N * K))))
+        w8 = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev).t() for _ in range(R)]
+        ours = [(packed, q, rs)] + [(packed.clone(), q.clone(), rs.clone()) for _ in range(R - 1)]
+        xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        sx = torch.rand(M, device=dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        t_lib = timed(lambda i: torch._int_mm(xq, w8[i % R]))
+        t_tl = timed(lambda i: tl.gemm_int8_rescale(xq, sx, *ours[i % R], out=y))
+        ops = 2.0 * M * N * K
+        print(json.dumps({"M": M, "K": K, "N": N, "torch_int_mm_us": round(t_lib, 1),
+                          "torch_int_mm_TOPs": round(ops / t_lib / 1e6, 1), "tl_gemm_us": round(t_tl, 1),
+                          "tl_gemm_TOPs": round(ops / t_tl / 1e6, 1), "tl_kernel": tl.last_kernel_name()}), flush=True)
+        del w8, ours, packed, q, rs
+        torch.cuda.empty_cache()
 
 
 SWEEP_BS = (1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48, 64, 96, 128, 192, 256, 384, 512)
