@@ -127,6 +127,8 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
         rows = _pmc_rows(path)
         gemv = [(n, v) for n, v in rows if "gemv_stream_kernel" in n or "gemv_ring_kernel" in n]
         gemm = [(n, v) for n, v in rows if "gemm_i8_kernel" in n]
+        # the steps come first; the GEMV launches of the launch-cost fit follow them
+        gemv = gemv[:len(gemm) // (2 * PRE_LAYERS) * DEC_LAYERS * len(DECODE_BS)]
         if not gemv or len(gemv) % (DEC_LAYERS * len(DECODE_BS)) or not gemm or len(gemm) % (2 * PRE_LAYERS):
             raise SystemExit(f"unexpected launch counts in {path}: {len(gemv)} GEMV, {len(gemm)} GEMM")
         for i, (name, v) in enumerate(gemv):
@@ -493,7 +495,7 @@ def library_reference(tl, torch, dev, n=20):
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
-    for (M, K, N) in ((512, 5120, 34816), (512, 17408, 5120), (2048, 5120, 34816)):
+    for (M, K, N) in ((512, 5120, 34816), (512, 17408, 5120), (2048, 5120, 34816), (4096, 8192, 8192)):
         L = synth.LayerInputs(0, 3, 1, K, N)
         codes = L.codes_torch(dev)
         scales = torch.from_numpy(L.scales()).to(dev)

@@ -13,25 +13,34 @@
 // 128 int32 accumulators per lane), so every expanded weight fragment feeds four
 // MFMAs.  The K loop steps one pair of 128-wide scale groups (8 MFMA k-steps).
 //
-// Pipeline, per pair p:
+// Two pipelines.  With at least two tiles per compute unit (512 or more), two
+// workgroups share each CU (256 registers per lane each), so that one's stalls
+// are covered by the other's MFMAs:
+//  * the activation tile of pair p+1 is loaded straight into the second of two
+//    LDS buffers (buffer loads with the LDS destination, 1 KB per instruction)
+//    while pair p is computed from the first; rows are unpadded and each 16-byte
+//    chunk c of row r sits at c ^ (r % 16), so the fragment reads of 16 rows
+//    hit 16 different bank groups; the reads are issued by hand with their own
+//    waits (the compiler would otherwise wait for every load before them);
+//  * packed weight words arrive in a two-deep register ring.
+// Otherwise one workgroup per CU with a deeper pipeline:
 //  * the activation tile of pair p sits in one of three LDS buffers; the one of
 //    pair p+1 is already complete, the one of pair p+2 is written half way
 //    through pair p from registers loaded one pair earlier;
-//  * packed weight words arrive in a three-deep register ring (pairs p, p+1,
-//    p+2 in flight) and are loaded straight from the 1 KB packed tiles: two
-//    16-byte loads per column per pair;
-//  * inside a pair, the LDS reads and the weight expansion of k-step s+1 are
-//    issued between the MFMAs of k-step s, so neither LDS latency nor the
-//    expansion sits on the MFMA chain; one barrier per pair.
+//  * packed weight words arrive in a four-deep register ring.
+// In both, weight words are loaded straight from the 1 KB packed tiles (two
+// 16-byte loads per column per pair), the LDS reads and the weight expansion of
+// k-step s+1 are issued between the MFMAs of k-step s, and there is one barrier
+// per pair.
 // The expansion code -> code*q is one v_perm_b32 per 4 weights: the selector
 // bytes are the 2-bit fields ((w >> 2r) & 0x03030303) and the table holds
 // {0, q, -, -q}.
 //
-// Work distribution: the tiles are dealt out in whole rounds of kSlots
-// workgroups (one per compute unit), each round XCD-aware so that the four
-// M-blocks of one weight strip run on one XCD and share its L2.  The tiles left
-// over for a last, partial round are either
-//  * cut into eight 32 x 128 sub-tiles (when at most kSlots / 8 are left), each a
+// Work distribution: the tiles are dealt out in whole rounds of workgroups (one
+// or two per compute unit), each round XCD-aware so that the M-blocks of a
+// weight strip run on one XCD and share its L2.  The tiles left over for a last,
+// partial round are either
+//  * cut into eight 32 x 128 sub-tiles (when at most 256 / 8 are left), each a
 //    workgroup of its own over the whole K: the same pipeline with one 32 x 32
 //    MFMA tile per wave; nothing to add up afterwards; or
 //  * split along K into S pieces; every piece stores its int32 partial tile to
@@ -55,7 +64,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kPairK = 2 * kGroup;        // k per pipeline stage: one pair of groups
 constexpr int kAStride = kPairK + 16;     // LDS row pitch in bytes (padding spreads banks)
-constexpr int kSlots = 256;               // workgroups per round: the compute units of gfx950
+constexpr int kSlots = 256;               // the compute units of gfx950
 constexpr int kXcds = 8;                  // workgroup i runs on XCD i % 8
 constexpr int kMaxSplit = 6;
 
@@ -76,6 +85,16 @@ constexpr int kBN = Big::BN;
 constexpr int kABuf = Big::ABuf;
 constexpr int kTileInts = Big::Ints;
 constexpr int kNarrowPerTile = (Big::BM / Narrow::BM) * (Big::BN / Narrow::BN);
+// Two pipelines (TWO selects): one workgroup per compute unit with three padded
+// activation stages in LDS staged through registers and a four-deep weight ring;
+// or two workgroups per compute unit (256 registers per lane each) with two
+// swizzled activation stages loaded straight into LDS and a two-deep weight ring.
+template <bool TWO>
+struct Pipe {
+  static constexpr int lds = (TWO ? 2 : 3) * kABuf;  // activation stages; also the epilogue staging room
+  static constexpr int per_cu = TWO ? 2 : 1;
+  static constexpr int turn = TWO ? 2 : 4;           // pairs per ring turn (the K loop pads to it)
+};
 
 static_assert(kTileInts == kThreads * 128, "128 accumulators per thread");
 
@@ -89,7 +108,9 @@ struct BStage {
 struct Schedule {
   int mb;         // M-blocks
   int tiles;      // MB * N-strips
-  int full;       // tiles computed whole, in rounds of kSlots (the rest are split or cut)
+  int two;        // 1: the two-workgroups-per-CU pipeline
+  int round;      // workgroups per whole round: kSlots times workgroups per CU
+  int full;       // tiles computed whole, in whole rounds (the rest are split or cut)
   int split;      // pieces per left-over tile along K (1: nothing is split)
   int narrow;     // 1: the left-over tiles are cut into kNarrowPerTile sub-tiles
   __host__ __device__ int64_t left() const { return split > 1 || narrow ? tiles - full : 0; }
@@ -129,11 +150,13 @@ struct Frame {
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 constexpr int kCoherent = 16;           // cache policy sc1: coherent across the XCDs' L2s
 
+// The row of every access is in the per-lane (VGPR) offset, which the buffer range
+// check covers; the scalar offset only moves along the row (p * 256 < K).
 template <int NP, int J>
 __device__ __forceinline__ void load_a(v4u (&a)[NP], const Frame<J> &f, int p) {
 #pragma unroll
   for (int i = 0; i < NP; ++i)
-    a[i] = __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.aoff, p * kPairK + i * f.astep, 0);
+    a[i] = __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.aoff + i * f.astep, p * kPairK, 0);
 }
 
 template <int J>
@@ -243,34 +266,40 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // each 32x32 tile, rows 8*(r/4) + 4*h + r%4: four consecutive rows per r/4, whose
 // token scales come from LDS in one 16-byte read.  A tile that lies inside
 // [M, N] takes the variant without per-element bounds tests.
-template <bool kCheck, bool kF32, int MT, int J>
+template <bool kCheck, bool kF32, bool kAcc, int MT, int J>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[MT][J], const float *s_tok,
                                          const float (&rsv)[J], int64_t m0, int64_t n0, int64_t M,
                                          int64_t N, int wave, int l32, int h, void *y,
                                          int32_t *acc_out) {
+  // the lane's first row (4 h) and column; element (r, 32 j) away sits r N + 32 j
+  // further, a uniform offset, so that only the two base pointers are per lane
+  const int64_t mb = m0 + 4 * h, nb = n0 + 32 * J * wave + l32;
+  char *yb = static_cast<char *>(y) + (mb * N + nb) * (kF32 ? 4 : 2);
+  int32_t *ab = kAcc ? acc_out + (mb * N + nb) : nullptr;
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int64_t n = n0 + 32 * J * wave + 32 * j + l32;
-    if (kCheck && n >= N) continue;
+    if (kCheck && nb + 32 * j >= N) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        const int row = 32 * mt + 8 * rq + 4 * h;
-        const v4f ts = *reinterpret_cast<const v4f *>(s_tok + row);
+        const v4f ts = *reinterpret_cast<const v4f *>(s_tok + 32 * mt + 8 * rq + 4 * h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + row + i;
-          if (kCheck && m >= M) continue;
+          const int r = 32 * mt + 8 * rq + i;
+          if (kCheck && mb + r >= M) continue;
           const int a = acc[mt][j][4 * rq + i];
           const float v = ((float)a * rsv[j]) * ts[i];
-          const int64_t o = m * N + n;
-          if (acc_out) acc_out[o] = a;
+          const int64_t off = int64_t(r) * N + 32 * j;
+          if (kAcc) ab[off] = a;
           if (kF32)
-            reinterpret_cast<float *>(y)[o] = v;
+            reinterpret_cast<float *>(yb)[off] = v;
           else
-            reinterpret_cast<uint16_t *>(y)[o] = float_to_bf16_bits(v);
+            reinterpret_cast<uint16_t *>(yb)[off] = float_to_bf16_bits(v);
         }
+        // one group of four rows at a time: keeps the live values within the
+        // register budget of the two-per-CU pipeline
+        __builtin_amdgcn_sched_barrier(0);
       }
   }
 }
@@ -279,16 +308,16 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[MT][J], const float *
 // activation buffers, free once the K loop is done) so that every lane stores 16
 // contiguous bytes of a row -- a wave writes whole rows -- instead of 2- or
 // 4-byte pieces down a column.  f32 output goes in two passes of 64 rows.
-template <bool kF32, int MT, int J>
+template <bool kF32, int MT, int J, int kStageCap>
 __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const float *s_tok,
                                              const float (&rsv)[J], int64_t m0, int64_t n0, int64_t N,
                                              int wave, int l32, int h, int tid, void *y, int8_t *stage) {
   constexpr int BM = Tile<MT, J>::BM, BN = Tile<MT, J>::BN;
   constexpr int ES = kF32 ? 4 : 2;         // bytes per output
   constexpr int PITCH = BN * ES + 16;      // LDS row pitch (the pad spreads the 4-row steps over banks)
-  constexpr int ROWS = BM * PITCH <= 3 * kABuf ? BM : BM / 2;  // rows per pass
+  constexpr int ROWS = BM * PITCH <= kStageCap ? BM : BM / 2;  // rows per pass
   constexpr int CPR = BN * ES / 16;        // 16-byte chunks per row
-  static_assert(ROWS * PITCH <= 3 * kABuf, "staging fits the activation buffers");
+  static_assert(ROWS * PITCH <= kStageCap, "staging fits the activation buffers");
   __syncthreads();  // every wave is done with the activation buffers
 #pragma unroll
   for (int pass = 0; pass < BM / ROWS; ++pass) {
@@ -324,12 +353,19 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const flo
   }
 }
 
+// The two-per-CU pipeline runs when there are at least two tiles per compute unit
+// (whole rounds of 512); smaller problems keep one deeper-pipelined workgroup per
+// CU.  Left-over tiles are cut or split so that the last round is at most one
+// workgroup per CU.
 inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   Schedule sc;
   sc.mb = int((M + kBM - 1) / kBM);
   sc.tiles = sc.mb * int((N + kBN - 1) / kBN);
+  sc.two = sc.tiles >= 2 * kSlots;
+  sc.round = sc.two ? 2 * kSlots : kSlots;
+  const int turn = sc.two ? Pipe<true>::turn : Pipe<false>::turn;
   sc.narrow = 0;
-  const int left = sc.tiles % kSlots;
+  const int left = sc.tiles % sc.round;
   int best = 1;
   if (left && left * kNarrowPerTile <= kSlots) {
     // a short last round: every left-over tile becomes eight sub-tile workgroups
@@ -339,10 +375,10 @@ inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
     return sc;
   }
   if (left) {
-    int64_t best_cost = (GP + 3) / 4 * 4;
+    int64_t best_cost = (GP + turn - 1) / turn * turn;
     for (int S = 2; S <= kMaxSplit && S * left <= kSlots && S <= GP; ++S) {
       const int64_t piece = (GP + S - 1) / S;
-      const int64_t cost = (piece + 3) / 4 * 4 + (S - 1);
+      const int64_t cost = (piece + turn - 1) / turn * turn + (S - 1);
       if (cost < best_cost) best_cost = cost, best = S;
     }
   }
@@ -363,10 +399,93 @@ struct GemmArgs {
   int32_t *acc_out, *part, *counters;
 };
 
+// ---------------------------------------------------------------------------
+// two-stage pipeline with activation stages loaded straight into LDS
+// ---------------------------------------------------------------------------
+// Stage layout: rows of 256 bytes, no padding; 16-byte chunk c of row r sits at
+// physical chunk c ^ (r & 15), so that 16 consecutive rows reading the same chunk
+// hit 16 different bank groups.
+__device__ __forceinline__ v4i lds_read16(uint32_t addr) {
+  v4i r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+template <int MT>
+__device__ __forceinline__ void read_a2(v4i (&af)[MT], uint32_t rowaddr, int xsw, int h, int s) {
+  const int c = 8 * (s >> 2) + (s & 3) + 4 * h;
+  const uint32_t a = rowaddr + 16 * uint32_t(c ^ xsw);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) af[mt] = lds_read16(a + 32 * 256 * mt);
+}
+
+template <int MT, int N>
+__device__ __forceinline__ void wait_a2(v4i (&af)[MT]) {
+  if constexpr (MT == 4)
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]) : "n"(N));
+  else if constexpr (MT == 2)
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(af[0]), "+v"(af[1]) : "n"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(af[0]) : "n"(N));
+}
+
+// the activation stage of pair p into LDS buffer buf: instruction j = wave + 4 i
+// covers rows 4 j .. 4 j + 3; lane l takes row 4 j + l / 16 and logical chunk
+// (l % 16) ^ (row % 16), the row's bytes at physical chunk l % 16
+template <int MT, int J>
+__device__ __forceinline__ void dma_a2(const Frame<J> &f, int8_t *buf, int p, int wave, int dvoff,
+                                       int64_t K) {
+#if __HIP_DEVICE_COMPILE__
+#pragma unroll
+  for (int i = 0; i < 2 * MT; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        f.ra, (__attribute__((address_space(3))) void *)(buf + 1024 * (wave + 4 * i)), 16,
+        dvoff + int(16 * K) * i, p * kPairK, 0, 0);
+#endif
+}
+
+template <int S, int MT, int J>
+__device__ __forceinline__ void pair_body2(int p, int k0, int plast, const Frame<J> &f, int8_t *sA,
+                                           uint32_t rowaddr, int xsw, int h, int wave, int dvoff, int64_t K,
+                                           BStage<J> (&ring)[2], v4i (&af)[2][MT], v4i (&bf)[2][J],
+                                           v16i (&acc)[MT][J]) {
+  constexpr int AB = Tile<MT, J>::BM * 256;
+  // the next pair's stage into the other buffer (every wave left it at the last barrier)
+  dma_a2<MT, J>(f, sA + (S ^ 1) * AB, min(max(p + 1, k0), plast), wave, dvoff, K);
+  const uint32_t cur = rowaddr + S * AB;
+  read_a2<MT>(af[0], cur, xsw, h, 0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s < 7) {
+      read_a2<MT>(af[(s + 1) & 1], cur, xsw, h, s + 1);
+      wait_a2<MT, MT>(af[s & 1]);
+    } else {
+      wait_a2<MT, 0>(af[s & 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(af[s & 1], bf[s & 1], acc);
+    if (s < 7)
+      fetch_b(bf[(s + 1) & 1], ring[S], s + 1);
+    else
+      fetch_b(bf[0], ring[S ^ 1], 0);
+#pragma unroll
+    for (int i = 0; i < MT * J; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (s == 7) load_b(ring[S], f, min(max(p + 2, k0), plast), p + 2 >= k0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // this wave's stage loads are done (the weight loads just issued may stay in flight)
+  __builtin_amdgcn_s_waitcnt(0x0F70 & ~0x0F | (4 * J));
+  __syncthreads();
+}
+
 // One workgroup tile of 32 MT x 128 J at (m0, n0) over the pairs [k0, k1).  A
 // piece of a K-split tile (piece >= 0, big tiles only) publishes its partial
 // tile and only the last piece to arrive runs the epilogue.
-template <int MT, int J>
+template <int MT, int J, bool TWO>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, int8_t *sA, float *s_tok,
                                          int *s_last, int64_t m0, int64_t n0, int k0, int k1, int tile,
                                          int piece, int slot) {
@@ -417,6 +536,30 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
 
+  if constexpr (TWO) {
+    // two LDS stages filled straight from memory, two weight slots; an even pair
+    // count (a leading zero-weight pair when odd)
+    const int p0 = k0 - ((k1 - k0) & 1);
+    const int plast = k1 - 1;
+    BStage<J> ring[2];
+    load_b(ring[0], f, min(max(p0, k0), plast), p0 >= k0);
+    load_b(ring[1], f, min(max(p0 + 1, k0), plast), p0 + 1 >= k0);
+    // DMA source offset of this lane: row 4 wave + lane / 16 (+ 16 i), logical chunk
+    const int rbase = 4 * wave + (lane >> 4);
+    const int dvoff = int(rbase * K) + 16 * ((lane & 15) ^ (rbase & 15));
+    dma_a2<MT, J>(f, sA, min(max(p0, k0), plast), wave, dvoff, K);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    const uint32_t rowaddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t *)sA + 256 * l32;
+    const int xsw = l32 & 15;
+    v4i af[2][MT], bf[2][J];
+    fetch_b(bf[0], ring[0], 0);
+    for (int p = p0; p < k1; p += 2) {
+      pair_body2<0, MT, J>(p, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
+      pair_body2<1, MT, J>(p + 1, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
+  } else {
   // The pair count is padded up to a multiple of 4 with leading zero-weight
   // pairs, so that the loop below only exits after a whole ring turn.
   // prologue: LDS buffers 0 and 1 <- pairs p0, p0+1; registers <- pair p0+2;
@@ -447,6 +590,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
     pair_body<1, MT, J>(p + 1, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
     pair_body<2, MT, J>(p + 2, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
     pair_body<3, MT, J>(p + 3, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+  }
   }
 
   if (piece >= 0) {
@@ -500,16 +644,24 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
 
   const bool whole = m0 + T::BM <= M && n0 + T::BN <= N;
   if (whole && !a.acc_out && N % 8 == 0) {  // rows of y start on 16-byte boundaries
-    if (a.y_dtype == TL_F32) epilogue_lds<true>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
-    else epilogue_lds<false>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
+    if (a.y_dtype == TL_F32) epilogue_lds<true, MT, J, Pipe<TWO>::lds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
+    else epilogue_lds<false, MT, J, Pipe<TWO>::lds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
     return;
   }
-  if (a.y_dtype == TL_F32) {
-    if (whole) epilogue<false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
-    else epilogue<true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+  // variants with and without the exact accumulators, so that no store sits
+  // behind a per-element branch (edge tiles, and rows not 16-byte aligned, check bounds)
+  const bool f32 = a.y_dtype == TL_F32;
+  if (a.acc_out) {
+    if (f32) {
+      if (whole) epilogue<false, true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+      else epilogue<true, true, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+    } else {
+      if (whole) epilogue<false, false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+      else epilogue<true, false, true>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+    }
   } else {
-    if (whole) epilogue<false, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
-    else epilogue<true, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, a.acc_out);
+    if (f32) epilogue<true, true, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, nullptr);
+    else epilogue<true, false, false>(acc, s_tok, rsv, m0, n0, M, N, wave, l32, h, a.y, nullptr);
   }
 }
 
@@ -521,13 +673,14 @@ __device__ __forceinline__ int xcd_item(int e, int total) {
   return (total / kXcds) * (e % kXcds) + e / kXcds;
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
+template <bool TWO>
+__global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int64_t M, int64_t K,
     int64_t N, const uint32_t *__restrict__ packed, const int8_t *__restrict__ q,
     const float *__restrict__ row_scale, void *__restrict__ y, int y_dtype,
     int32_t *__restrict__ acc_out, int32_t *__restrict__ part, int32_t *__restrict__ counters,
     Schedule sc) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[3 * kABuf];
+  __shared__ __attribute__((aligned(16))) int8_t sA[Pipe<TWO>::lds];
   __shared__ __attribute__((aligned(16))) float s_tok[kBM];
   __shared__ int s_last;
   const GemmArgs a{xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters};
@@ -543,14 +696,14 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
     const int64_t m0 = int64_t(tile % sc.mb) * kBM + Narrow::BM * (u % kRowCuts);
     const int64_t n0 = int64_t(tile / sc.mb) * kBN + Narrow::BN * (u / kRowCuts);
     if (m0 >= M || n0 >= N) return;  // the whole sub-tile lies past the output
-    run_tile<Narrow::BM / 32, Narrow::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
+    run_tile<Narrow::BM / 32, Narrow::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
     return;
   }
   int tile, piece = -1, slot = 0, k0 = 0, k1 = GP;
   if (g < sc.full) {
-    const int round = g / kSlots, u = g % kSlots;
-    tile = (kSlots % kXcds == 0 && sc.full - round * kSlots >= kSlots)
-               ? round * kSlots + (kSlots / kXcds) * (u % kXcds) + u / kXcds
+    const int round = g / sc.round, u = g % sc.round;
+    tile = (sc.round % kXcds == 0 && sc.full - round * sc.round >= sc.round)
+               ? round * sc.round + (sc.round / kXcds) * (u % kXcds) + u / kXcds
                : g;
   } else {
     slot = xcd_item(g - sc.full, int(sc.grid() - sc.full));
@@ -561,7 +714,7 @@ __global__ __launch_bounds__(kThreads) void gemm_i8_kernel(
   }
   const int64_t m0 = int64_t(tile % sc.mb) * kBM;
   const int64_t n0 = int64_t(tile / sc.mb) * kBN;
-  run_tile<Big::BM / 32, Big::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
+  run_tile<Big::BM / 32, Big::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
 }
 
 // Workspace layout, the same for every shape so that one workspace serves calls
@@ -589,10 +742,16 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
     part = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
   }
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
-                     M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
-  set_last_kernel(s.narrow ? "gemm_i8_mfma32_128x256_narrowtail"
-                           : s.split > 1 ? "gemm_i8_mfma32_128x256_splitk" : "gemm_i8_mfma32_128x256");
+  if (s.two)
+    hipLaunchKernelGGL(gemm_i8_kernel<true>, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
+                       M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
+  else
+    hipLaunchKernelGGL(gemm_i8_kernel<false>, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
+                       M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
+  static const char *names[2][3] = {
+      {"gemm_i8_mfma32_128x256", "gemm_i8_mfma32_128x256_splitk", "gemm_i8_mfma32_128x256_narrowtail"},
+      {"gemm_i8_mfma32_128x256_lds2", "gemm_i8_mfma32_128x256_lds2_splitk", "gemm_i8_mfma32_128x256_lds2_narrowtail"}};
+  set_last_kernel(names[s.two][s.narrow ? 2 : s.split > 1 ? 1 : 0]);
   return hipGetLastError();
 }
 

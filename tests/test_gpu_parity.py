@@ -322,6 +322,22 @@ def test_gemm_narrow_tail(tl, M, K, N):
     assert tl.last_kernel_name().endswith("narrowtail")
 
 
+@pytest.mark.parametrize("M,K,N", [(2000, 384, 8200), (1100, 1280, 30000)])
+def test_gemm_two_per_cu_ragged(tl, M, K, N):
+    """At least two tiles per compute unit: the two-workgroups-per-CU pipeline,
+    with ragged last M-block and N-strip, an odd group count (K = 384) and a
+    left-over round (cut into sub-tiles, or split along K)."""
+    d = dev()
+    rng = np.random.default_rng(M + K + N)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.exp(rng.standard_normal(M)).astype(np.float32)
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "two per CU")
+    assert "_lds2" in tl.last_kernel_name()
+
+
 def test_gemm_workspace_reused_across_shapes(tl):
     """One workspace, K-split GEMMs of different shapes in turn (64 and 128 split
     tiles): the counters of one shape never overlap the partials of another, and
