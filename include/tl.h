@@ -269,7 +269,7 @@ int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *s
  *                (exact; |acc| <= K * 127^2, so K <= 133143 keeps it in int32)
  * workspace      device scratch of at least tl_gemm_workspace_size(M, K, N)
  *                bytes (may be NULL when that size is 0).  Layout: 256 int32
- *                counters (one per K-split tile; at most 255 are ever used),
+ *                counters (one per K-split tile; at most 256 are ever used),
  *                then the int32 partial tiles of the K-split work.  It must be
  *                zero-filled before its first use; every call leaves the
  *                counters at zero again, so one workspace can be reused, also
@@ -277,7 +277,8 @@ int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *s
  *                must not share one.
  * The size depends only on (M, K, N): the schedule is fixed for the 256
  * compute units of gfx950 (whole rounds of 128 x 256 tiles, the left-over
- * tiles split along K).
+ * tiles split along K or cut into sub-tiles; with fewer 128 x 256 tiles than
+ * compute units, 128 x 128 tiles split along K into up to 6 pieces).
  * Requires K > 0, K % 128 == 0, K <= 133120.
  */
 size_t tl_gemm_workspace_size(int64_t M, int64_t K, int64_t N);
@@ -298,8 +299,8 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
  *   [P1] "前提" (the layer), "4. 効いた高速化" (the prefill path); the choice by
  *   token count mirrors the page's decode / prefill split.
  * tl_linear_path: up to 16 tokens the GEMV; 17..64 tokens the GEMV while
- * ceil(T/16) * ceil(N/64) <= 640 (its chunk workgroups fit in about 2.5 rounds of
- * the 256 compute units), else the int8 path; above 64 tokens the int8 path.
+ * ceil(T/16) * N * K <= 3 * 2^26 (every 16-token chunk streams all weights
+ * again), else the int8 path; above 64 tokens the int8 path.
  * The rule follows a measured token sweep of both paths at the qkv
  * (5120 -> 10240), gate_up (5120 -> 34816) and down (17408 -> 5120) shapes.
  * in  x          bf16 [T, K] raw layer input; signs as in tl_hadamard_blk

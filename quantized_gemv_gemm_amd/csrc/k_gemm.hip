@@ -49,6 +49,9 @@
 //    independent).
 // The left-over work is dealt out XCD by XCD (workgroup i runs on XCD i % 8), so
 // that the pieces or sub-tiles of one weight strip share an L2.
+// With fewer 128 x 256 tiles than compute units (few tokens, or a narrow output
+// with long K), the whole problem takes 128 x 128 tiles (each wave 128 x 32) on
+// the two-per-CU pipeline, split along K into as many pieces as fit 512 slots.
 // No workgroup ever waits for another.
 #include <algorithm>
 
@@ -80,6 +83,7 @@ struct Tile {
 };
 typedef Tile<4, 2> Big;     // 128 x 256: the tile of the whole rounds
 typedef Tile<1, 1> Narrow;  // 32 x 128: an eighth of a big tile, for a short last round
+typedef Tile<4, 1> Mid;     // 128 x 128: the tile of problems with fewer big tiles than CUs
 constexpr int kBM = Big::BM;
 constexpr int kBN = Big::BN;
 constexpr int kABuf = Big::ABuf;
@@ -113,7 +117,8 @@ struct Schedule {
   int full;       // tiles computed whole, in whole rounds (the rest are split or cut)
   int split;      // pieces per left-over tile along K (1: nothing is split)
   int narrow;     // 1: the left-over tiles are cut into kNarrowPerTile sub-tiles
-  __host__ __device__ int64_t left() const { return split > 1 || narrow ? tiles - full : 0; }
+  int mid;        // 1: every tile is a Mid tile (mb, tiles count Mid tiles), split `split` ways
+  __host__ __device__ int64_t left() const { return split > 1 || narrow || mid ? tiles - full : 0; }
   __host__ __device__ int64_t grid() const { return full + left() * (narrow ? kNarrowPerTile : split); }
 };
 
@@ -354,13 +359,35 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const flo
 }
 
 // The two-per-CU pipeline runs when there are at least two tiles per compute unit
-// (whole rounds of 512); smaller problems keep one deeper-pipelined workgroup per
-// CU.  Left-over tiles are cut or split so that the last round is at most one
-// workgroup per CU.
+// (whole rounds of 512); otherwise one deeper-pipelined workgroup per CU.
+// Left-over tiles are cut or split so that the last round is at most one
+// workgroup per CU.  Problems with fewer big tiles than CUs (few tokens, or a
+// narrow output with long K) take 128 x 128 tiles on the two-per-CU pipeline
+// instead, split along K into as many pieces as fill at most 512 slots: twice the
+// workgroups of the same size at no extra partial-tile bytes (S partial tiles of
+// half the size), each CU interleaving two of them.
 inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   Schedule sc;
   sc.mb = int((M + kBM - 1) / kBM);
   sc.tiles = sc.mb * int((N + kBN - 1) / kBN);
+  sc.mid = 0;
+  if (sc.tiles < kSlots) {
+    const int mmb = int((M + Mid::BM - 1) / Mid::BM);
+    const int mtiles = mmb * int((N + Mid::BN - 1) / Mid::BN);
+    if (mtiles <= 2 * kSlots) {
+      int S = 1;
+      while (S < kMaxSplit && (S + 1) * mtiles <= 2 * kSlots && S + 1 <= GP) ++S;
+      sc.mid = 1;
+      sc.two = 1;
+      sc.round = 2 * kSlots;
+      sc.mb = mmb;
+      sc.tiles = mtiles;
+      sc.full = 0;
+      sc.split = S;
+      sc.narrow = 0;
+      return sc;
+    }
+  }
   sc.two = sc.tiles >= 2 * kSlots;
   sc.round = sc.two ? 2 * kSlots : kSlots;
   const int turn = sc.two ? Pipe<true>::turn : Pipe<false>::turn;
@@ -688,6 +715,20 @@ __global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
 
   // which tile and which K range this workgroup computes
   const int g = blockIdx.x;
+  if constexpr (TWO) {
+    if (sc.mid) {
+      // Mid tile e / S, K piece e % S (no piece when S = 1)
+      const int e = xcd_item(g, int(sc.grid()));
+      const int S = sc.split;
+      const int tile = e / S, piece = S > 1 ? e % S : -1;
+      const int k0 = S > 1 ? int(int64_t(GP) * piece / S) : 0;
+      const int k1 = S > 1 ? int(int64_t(GP) * (piece + 1) / S) : GP;
+      const int64_t m0 = int64_t(tile % sc.mb) * Mid::BM;
+      const int64_t n0 = int64_t(tile / sc.mb) * Mid::BN;
+      run_tile<Mid::BM / 32, Mid::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);
+      return;
+    }
+  }
   if (g >= sc.full && sc.narrow) {
     // sub-tile u of a left-over tile: rows 32 (u % 4), columns 128 (u / 4) of it
     const int e = xcd_item(g - sc.full, int(sc.grid() - sc.full));
@@ -718,8 +759,9 @@ __global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
 }
 
 // Workspace layout, the same for every shape so that one workspace serves calls
-// of different shapes: kSlots int32 counters (one per possible left-over tile;
-// fewer than kSlots tiles are ever left over), then the int32 partial tiles.
+// of different shapes: kSlots int32 counters (one per possible split tile; fewer
+// than kSlots tiles are ever split: at most 256 / S left-over big tiles, or at
+// most 512 / S Mid tiles), then the int32 partial tiles.
 constexpr size_t kCounterBytes = kSlots * sizeof(int32_t);
 
 }  // namespace
@@ -728,7 +770,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   const Schedule s = make_schedule(M, N, (K / kGroup + 1) / 2);
   if (s.split <= 1) return 0;
-  return kCounterBytes + size_t(s.left() * s.split) * kTileInts * 4;
+  return kCounterBytes + size_t(s.left() * s.split) * (s.mid ? Mid::Ints : kTileInts) * 4;
 }
 
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
@@ -751,7 +793,10 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
   static const char *names[2][3] = {
       {"gemm_i8_mfma32_128x256", "gemm_i8_mfma32_128x256_splitk", "gemm_i8_mfma32_128x256_narrowtail"},
       {"gemm_i8_mfma32_128x256_lds2", "gemm_i8_mfma32_128x256_lds2_splitk", "gemm_i8_mfma32_128x256_lds2_narrowtail"}};
-  set_last_kernel(names[s.two][s.narrow ? 2 : s.split > 1 ? 1 : 0]);
+  if (s.mid)
+    set_last_kernel(s.split > 1 ? "gemm_i8_mfma32_128x128_lds2_splitk" : "gemm_i8_mfma32_128x128_lds2");
+  else
+    set_last_kernel(names[s.two][s.narrow ? 2 : s.split > 1 ? 1 : 0]);
   return hipGetLastError();
 }
 

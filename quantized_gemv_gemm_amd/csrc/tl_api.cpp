@@ -354,14 +354,15 @@ LinearLayout linear_layout(int64_t T, int64_t K, int64_t N) {
 }  // namespace
 
 int tl_linear_path(int64_t T, int64_t K, int64_t N) {
-  (void)K;
   if (T <= tl::kTokChunk) return TL_PATH_GEMV;
   if (T > tl::kGemvMaxTokens) return TL_PATH_INT8;
   // 17..64 tokens: the GEMV runs one chunk of 16 tokens per grid row, each
-  // streaming the weights again; it stays ahead while its workgroups (one per 64
-  // rows and chunk) fit in about 2.5 rounds of the 256 compute units.
-  const int64_t wg = tl::limb_chunks(T) * ((N + 63) / 64);
-  return wg <= 640 ? TL_PATH_GEMV : TL_PATH_INT8;
+  // streaming all N x K weights again, while the int8 path's time hardly grows
+  // with T at this size; the GEMV stays ahead up to about 3 x 2^26 streamed
+  // weights (qkv 5120 x 10240: three chunks; down 17408 x 5120: two; gate_up
+  // 5120 x 34816: none beyond the first).
+  const int64_t streamed = tl::limb_chunks(T) * N * K;
+  return streamed <= (int64_t(3) << 26) ? TL_PATH_GEMV : TL_PATH_INT8;
 }
 
 size_t tl_linear_workspace_size(int64_t T, int64_t K, int64_t N) {

@@ -126,7 +126,8 @@ def test_gemm_rejections():
     assert L.tl_gemm_int8_rescale(*args(dt=3)) == 4
     assert L.tl_gemm_int8_rescale(*args(y=None)) == 1
     assert L.tl_gemm_int8_rescale(*args(acc=ODD, y=ctypes.c_void_p(0xA0000000))) == 3
-    assert L.tl_gemm_int8_rescale(*args(y=FAKE)) == 8
+    assert L.tl_gemm_int8_rescale(*args(y=FAKE, K=128)) == 8   # one pair of groups: no workspace
+    assert L.tl_gemm_int8_rescale(*args(y=FAKE)) == 7            # 8 x 1024 x 256 is split along K
     assert L.tl_gemm_int8_rescale(*args(M=0)) == 0
     # 512 x 40960 leaves 128 of 640 tiles for a last round: they are split along K;
     # 512 x 34816 leaves 32 of 544, cut into sub-tiles that need no workspace
@@ -171,17 +172,18 @@ def test_fused_input_rejections():
 
 
 def test_linear_path_rule():
-    """Up to 16 tokens the GEMV; 17..64 while ceil(T/16) ceil(N/64) <= 640; above 64 the int8 path."""
+    """Up to 16 tokens the GEMV; 17..64 while ceil(T/16) N K <= 3 * 2^26; above 64 the int8 path."""
     P = tl.linear_path
     for T in (0, 1, 8, 16):
         assert P(T, 5120, 34816) == tl.PATH_GEMV and P(T, 17408, 1 << 20) == tl.PATH_GEMV
-    assert P(64, 5120, 10240) == tl.PATH_GEMV      # 4 x 160 = 640 workgroups
-    assert P(64, 17408, 5120) == tl.PATH_GEMV
-    assert P(17, 5120, 20480) == tl.PATH_GEMV      # 2 x 320
-    assert P(17, 5120, 20544) == tl.PATH_INT8      # 2 x 321
-    assert P(32, 5120, 34816) == tl.PATH_INT8      # gate_up: 2 x 544
+    assert P(48, 5120, 10240) == tl.PATH_GEMV      # qkv: 3 chunks x 52.4e6 weights
+    assert P(49, 5120, 10240) == tl.PATH_INT8      # 4 chunks
+    assert P(32, 17408, 5120) == tl.PATH_GEMV      # down: 2 chunks x 89.1e6
+    assert P(33, 17408, 5120) == tl.PATH_INT8
+    assert P(17, 5120, 34816) == tl.PATH_INT8      # gate_up: 2 chunks x 178e6
+    assert P(17, 1024, 98304) == tl.PATH_GEMV      # exactly 3 * 2^26 streamed weights
+    assert P(17, 1024, 98305) == tl.PATH_INT8
     assert P(65, 1024, 64) == tl.PATH_INT8 and P(512, 5120, 10240) == tl.PATH_INT8
-
 
 def test_linear_rejections():
     L = tl.lib()

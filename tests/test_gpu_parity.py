@@ -307,7 +307,7 @@ def test_gemm_ragged(tl, M, K, N):
     _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "ragged")
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 256, 22940), (130, 384, 4000)])
+@pytest.mark.parametrize("M,K,N", [(300, 256, 22940), (130, 384, 32800)])
 def test_gemm_narrow_tail(tl, M, K, N):
     """A short last round cut into 32 x 128 sub-tiles, some of them partly or wholly
     past M and N (300 rows = 2 whole M-blocks + 44 rows; a ragged last strip)."""
@@ -336,6 +336,23 @@ def test_gemm_two_per_cu_ragged(tl, M, K, N):
     packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
     _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "two per CU")
     assert "_lds2" in tl.last_kernel_name()
+
+
+@pytest.mark.parametrize("M,K,N", [(512, 17408, 5120), (130, 2048, 1000), (33, 384, 4000), (200, 640, 40),
+                                   (64, 128, 700)])
+def test_gemm_mid_tiles(tl, M, K, N):
+    """Fewer 128 x 256 tiles than compute units: 128 x 128 tiles, two per CU, split
+    along K (down at 512 tokens: 160 tiles x 3 pieces; 16 tiles x 6; ragged M and
+    N; an odd group count; N narrower than a tile; one pair of groups, no split)."""
+    d = dev()
+    rng = np.random.default_rng(M + K + N + 7)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    xq = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.exp(rng.standard_normal(M)).astype(np.float32)
+    packed, q, rs = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "mid tiles")
+    assert tl.last_kernel_name().startswith("gemm_i8_mfma32_128x128_lds2")
 
 
 def test_gemm_workspace_reused_across_shapes(tl):
