@@ -376,6 +376,23 @@ def main():
         xr_half = torch.empty((T, 512), dtype=torch.float32, device=dev)
         split_us[f"half_T{T}"] = round(run_time(lambda: tl.hadamard_half(xs[:, 512:1024], u=u)) * 1e3, 2)
         split_us[f"join_T{T}"] = round(run_time(lambda: tl.hadamard_join(u, u, 1, out=xr_half)) * 1e3, 2)
+    # Context for the per-launch floor, timed the same way: a one-element launch
+    # (dispatch and completion only), and the vendor library copying the qkv
+    # layer's packed codes (N K / 4 bytes read and written), over the same
+    # rotating copies.
+    one = torch.zeros((1,), dtype=torch.float32, device=dev)
+    codes_dst = torch.empty_like(qkv[0][0])
+    kq = [0]
+
+    def copy_codes():
+        codes_dst.copy_(qkv[kq[0] % len(qkv)][0])
+        kq[0] += 1
+    floor = {"empty_launch_us": round(run_time(lambda: one.add_(1.0)) * 1e3, 2)}
+    t_copy = run_time(copy_codes, n=DEC_LAYERS * 4) * 1e-3
+    nb = 2 * codes_dst.numel() * 4
+    floor["library_copy_codes"] = {"bytes_moved": int(nb), "us": round(t_copy * 1e6, 2),
+                                   "GBps": round(nb / t_copy / 1e9, 1)}
+    del codes_dst
     gc.enable()
 
     if os.environ.get("BENCH_DEBUG"):
@@ -455,6 +472,7 @@ def main():
             "prefill_rotate_quant_m512": {k: round((3 * PREFILL_M * pre_k[k] + 4 * PREFILL_M) /
                                                    (float(np.mean(v)) * 1e-3) / 1e9, 1)
                                           for k, v in quant_ms.items()}},
+        "launch_floor": floor,
         "input_kernels_us": {
             "decode_rotate_prep": {str(b): round(float(np.mean(prep_ms[b])) * 1e3, 2) for b in DECODE_BS},
             "prefill_rotate_quant_m512": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in quant_ms.items()},
