@@ -243,6 +243,13 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
  *     tl_gemv_prepare_x   == tl_hadamard_blk then tl_gemv_prepare
  *     tl_gemv_ternary_x   == tl_hadamard_blk then tl_gemv_ternary
  *     tl_quant_act_int8_x == tl_hadamard_blk then tl_quant_act_int8
+ *   except tl_gemv_ternary_x (and the GEMV path of tl_linear_apply) for one
+ *   token with N <= 12288 or two tokens with N <= 6144, and K <= 6144: there a
+ *   single kernel rotates, splits into limbs and runs the GEMV, each workgroup
+ *   rotating the blocks it needs, with the limbs scaled per 1024-block instead
+ *   of per token; its error against the exact layer is the same (about 3e-5)
+ *   but its output is not bit-identical to the sequence, and the workspace
+ *   (still required) is not used.
  * in  x       bf16 [b or T, K] raw layer input; signs as in tl_hadamard_blk.
  * Requires K % 1024 == 0 and K <= 65536 (TL_ERR_UNSUPPORTED above: use the
  * unfused calls); other arguments as in the unfused entry points.

@@ -41,6 +41,7 @@
 #include <mutex>
 #include <tuple>
 
+#include "rotate_dev.h"
 #include "tl_device.h"
 
 namespace tl {
@@ -972,6 +973,185 @@ void launch_q8_n(const Q8Plan &p, const Q8Args &a) {
   else launch_q8_p<RB, 4, ALDS>(p, a);
 }
 
+// --------------------------------------------------------------------------
+// gemv_rot: rotation, limbs and GEMV in one launch, for one or two tokens
+// --------------------------------------------------------------------------
+// Wave w of a workgroup owns Hadamard block w (1024 k, four group pairs) for the
+// workgroup's 16 RB rows.  It requests its block of x, the block's 8 group
+// scales of those rows (one 16-byte piece per row, straight into LDS) and its
+// four pairs of weight tiles, all at once; rotates the block for each token as
+// soon as x lands (binary64, exact, rounded once to f32 -- the same arithmetic
+// as tl_hadamard_blk); splits each token's block into two int8 limbs against the
+// block's own |x|max (sigma per token and block instead of per token); stages
+// the limbs in its own LDS (paired-limb rows, reusing the rotation scratch) and
+// runs its pairs as the tiles land.  Its partial sums, times the block's sigma,
+// are added across the waves.  Every workgroup rotates the blocks it needs
+// itself: no limbs in memory, no second launch, no barrier before the MFMAs.
+constexpr int kRotScratchBytes = kRotLds * 8;              // rotate_block_raw's LDS, per wave
+constexpr int kRotWaveBytes = kRotScratchBytes + 1024;     // + the wave's scale pieces
+constexpr int kRotLimbPitch = kHBlock + 16;                // limb row pitch in LDS
+constexpr int kRotMaxBlocks = 6;                           // waves per workgroup (LDS <= 64 KB)
+static_assert(4 * kRotLimbPitch <= kRotScratchBytes, "two tokens' limb rows fit the scratch");
+
+__host__ __device__ constexpr int rot_lds_bytes(int nblk, int rb) {
+  return nblk * kRotWaveBytes + (nblk > 1 ? nblk - 1 : 1) * rb * 2 * 64 * 4;
+}
+
+template <int RB, int B>
+__global__ __launch_bounds__(64 * kRotMaxBlocks) void gemv_rot_kernel(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ signs, int64_t K, int64_t N,
+    const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales, void *__restrict__ y,
+    int y_dtype) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int W = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, qd = lane >> 4;
+  const int G = int(K / kGroup), GP = G >> 1;
+  const int64_t NB = (N + 15) >> 4;
+  const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
+  char *wl = smem + wave * kRotWaveBytes;
+  double *scratch = reinterpret_cast<double *>(wl);
+  int8_t *lx = reinterpret_cast<int8_t *>(wl);  // limb rows, once the rotations are done
+  char *ls = wl + kRotScratchBytes;
+  float *red = reinterpret_cast<float *>(smem + W * kRotWaveBytes);
+  const int blk = wave;
+
+  // 1. loads, in this order: x (waited for first), scale pieces, weight tiles
+  RotRaw raw[B];
+#pragma unroll
+  for (int t = 0; t < B; ++t)
+    rotate_load(x + t * K + int64_t(kHBlock) * blk, signs ? signs + int64_t(kHBlock) * blk : nullptr,
+                lane, raw[t]);
+  asm volatile("" ::: "memory");
+  {
+    // lane r < 16 RB: the 8 scales of row n0 + r in this block (rows past N and
+    // lanes past 16 RB read a clamped, valid row; those bytes are never used)
+    const int64_t r = min(n0 + min(lane, 16 * RB - 1), N - 1);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(scales) + (r * G + 8 * blk) * 2,
+                                     (__attribute__((address_space(3))) void *)ls, 16, 0, 0);
+  }
+  asm volatile("" ::: "memory");
+  uint4 wv[4][RB];
+#pragma unroll
+  for (int pi = 0; pi < 4; ++pi)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      wv[pi][rb] = load_tile(packed, min(int64_t(blockIdx.x) * RB + rb, NB - 1), GP, 4 * blk + pi, lane);
+  asm volatile("" ::: "memory");
+
+  // 2. rotation and limbs (rotate_block_raw waits for its own x loads)
+  float out[B][kRotEPT];
+  float sig[B];
+#pragma unroll
+  for (int t = 0; t < B; ++t) {
+    rotate_block_raw(raw[t], signs != nullptr, scratch, lane, out[t]);
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRotEPT; ++j) m = fmaxf(m, fabsf(out[t][j]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    sig[t] = m / kLimbRange;
+    const float inv = m > 0.0f ? kLimbRange / m : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kRotEPT; ++j) out[t][j] *= inv;
+  }
+  // limb rows (hi of every token, then lo) over the scratch, element lane + 64 j
+#pragma unroll
+  for (int t = 0; t < B; ++t)
+#pragma unroll
+    for (int j = 0; j < kRotEPT; ++j) {
+      int q = (int)rintf(out[t][j]);
+      q = q > 32639 ? 32639 : (q < -32639 ? -32639 : q);
+      const int hi = (q + 128) >> 8;  // floor division: lo lands in [-128, 127]
+      lx[t * kRotLimbPitch + lane + 64 * j] = int8_t(hi);
+      lx[(B + t) * kRotLimbPitch + lane + 64 * j] = int8_t(q - 256 * hi);
+    }
+  rot_wave_sync();
+  // the scale pieces have landed once only the weight loads are outstanding
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm<4 * RB>());
+
+  // 3. the block's four pairs (paired-limb A rows: hi/lo of tokens 0, 1)
+  const int tok = lp_token(col);
+  const int arow = (col & 1) * B + (tok < B ? tok : B - 1);
+  const int8_t *lah = lx + arow * kRotLimbPitch + 32 * qd;
+  float acc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[rb][i] = 0.0f;
+#pragma unroll
+  for (int pi = 0; pi < 4; ++pi) {
+    v4i ah[2][2], al[2][2];
+    uint32_t sb[2][RB];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int gl = 2 * pi + gi;  // group inside the block
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ah[gi][h] = lds_read16(lah + 128 * gl + 16 * h);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sb[gi][rb] = lds_read_u16(ls + 16 * (16 * rb + col) + 2 * gl);
+    }
+    lds_wait<RB>(ah, al, sb, true);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) al[gi][h] = ah[gi][h];
+    float sv[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      sv[0][rb] = half_bits_to_float(uint16_t(sb[0][rb]));
+      sv[1][rb] = half_bits_to_float(uint16_t(sb[1][rb]));
+    }
+    pair_mfma<RB, 2, true>(ah, al, wv[pi], sv, acc);
+  }
+
+  // 4. the block's sigma (accumulator i holds token 2 qd + i), the 1/64 of the
+  //    unpacked codes, then the sum over the waves
+  const float c0 = sig[min(2 * qd, B - 1)] * (1.0f / 64.0f);
+  const float c1 = sig[min(2 * qd + 1, B - 1)] * (1.0f / 64.0f);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    acc[rb][0] *= c0;
+    acc[rb][1] *= c1;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) red[(((wave - 1) * RB + rb) * 2 + i) * 64 + lane] = acc[rb][i];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  for (int w = 1; w < W; ++w)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[rb][i] += red[(((w - 1) * RB + rb) * 2 + i) * 64 + lane];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = 2 * qd + i;
+    if (t >= B) continue;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int64_t n = n0 + 16 * rb + col;
+      if (n >= N) continue;
+      if (y_dtype == TL_F32)
+        reinterpret_cast<float *>(y)[int64_t(t) * N + n] = acc[rb][i];
+      else
+        reinterpret_cast<uint16_t *>(y)[int64_t(t) * N + n] = float_to_bf16_bits(acc[rb][i]);
+    }
+  }
+}
+
+template <int RB, int B>
+void launch_rot_t(int nblk, const uint16_t *x, const int8_t *signs, int64_t K, int64_t N,
+                  const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                  hipStream_t stream) {
+  const dim3 grid(unsigned((N + 16 * RB - 1) / (16 * RB)));
+  hipLaunchKernelGGL((gemv_rot_kernel<RB, B>), grid, dim3(64 * nblk), rot_lds_bytes(nblk, RB), stream, x,
+                     signs, K, N, packed, scales, y, y_dtype);
+}
+
 }  // namespace
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
@@ -1036,6 +1216,35 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
   else if (p.rb == 2) launch_ring_r<2>(p, grid, a);
   else launch_ring_r<1>(p, grid, a);
   set_last_kernel(p.name);
+  return hipGetLastError();
+}
+
+// The one-launch path pays for its redundant rotations (every workgroup rotates
+// every block of every token) with fewer launches and no limb round trip; it is
+// ahead while the workgroups are few: measured (device time, qkv-like K = 5120)
+// one token up to N = 10240 (9.1 against 11.0 us for prep + GEMV at N = 10240,
+// 6.7 against 9.6 at 5120, behind at 34816), two tokens up to N = 5120.
+bool gemv_rot_supported(int64_t b, int64_t K, int64_t N) {
+  if (K <= 0 || K % kHBlock || K / kHBlock > kRotMaxBlocks) return false;
+  return (b == 1 && N <= 12288) || (b == 2 && N <= 6144);
+}
+
+hipError_t launch_gemv_rot(const uint16_t *x, int64_t b, int64_t K, int64_t N, const int8_t *signs,
+                           const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                           hipStream_t stream) {
+  if (!gemv_rot_supported(b, K, N)) return hipErrorInvalidValue;
+  const int nblk = int(K / kHBlock);
+  const bool two_rb = N > 4096;  // 16 or 32 rows per workgroup: at most 256 or 384 workgroups
+  (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
+  if (b == 1) {
+    if (two_rb) launch_rot_t<2, 1>(nblk, x, signs, K, N, packed, scales, y, y_dtype, stream);
+    else launch_rot_t<1, 1>(nblk, x, signs, K, N, packed, scales, y, y_dtype, stream);
+  } else {
+    if (two_rb) launch_rot_t<2, 2>(nblk, x, signs, K, N, packed, scales, y, y_dtype, stream);
+    else launch_rot_t<1, 2>(nblk, x, signs, K, N, packed, scales, y, y_dtype, stream);
+  }
+  static const char *names[2][2] = {{"gemv_rot_rb1_b1", "gemv_rot_rb1_b2"}, {"gemv_rot_rb2_b1", "gemv_rot_rb2_b2"}};
+  set_last_kernel(names[two_rb][b - 1]);
   return hipGetLastError();
 }
 

@@ -241,6 +241,8 @@ int tl_gemv_ternary_x(const uint16_t *x, int64_t b, int64_t K, int64_t N, const 
   Span out[] = {{y, ysz}, {workspace, need}};
   if (any_alias(in, 4, out, 2)) return TL_ERR_ALIAS;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (tl::gemv_rot_supported(b, K, N))
+    return from_hip(tl::launch_gemv_rot(x, b, K, N, signs, packed, scales, y, y_dtype, st));
   hipError_t e = tl::launch_gemv_prepare_rotated(x, b, K, signs, workspace, st);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype, st));
@@ -395,6 +397,8 @@ int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const in
   hipStream_t st = static_cast<hipStream_t>(stream);
   char *ws = static_cast<char *>(workspace);
   if (l.path == TL_PATH_GEMV) {
+    if (tl::gemv_rot_supported(T, K, N))
+      return from_hip(tl::launch_gemv_rot(x, T, K, N, signs, packed, scales, y, y_dtype, st));
     void *gw = ws + kLinCounters;
     hipError_t e = tl::launch_gemv_prepare_rotated(x, T, K, signs, gw, st);
     if (e != hipSuccess) return from_hip(e);

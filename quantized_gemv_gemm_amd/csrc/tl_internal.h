@@ -66,6 +66,12 @@ hipError_t launch_quant_x(const uint16_t *x, int64_t T, int64_t K, const int8_t 
 hipError_t launch_gemv_prepare_rotated(const uint16_t *x, int64_t b, int64_t K, const int8_t *signs,
                                        void *workspace, hipStream_t stream);
 
+// rotation + limbs + GEMV in one launch for one or two tokens (k_gemv.hip)
+bool gemv_rot_supported(int64_t b, int64_t K, int64_t N);
+hipError_t launch_gemv_rot(const uint16_t *x, int64_t b, int64_t K, int64_t N, const int8_t *signs,
+                           const uint32_t *packed, const uint16_t *scales, void *y, int y_dtype,
+                           hipStream_t stream);
+
 // decode GEMV against int8 activations (k_gemv.hip)
 bool gemv_q8_supported(int64_t b, int64_t K, int64_t N);
 hipError_t launch_gemv_q8(const int8_t *xq, const float *tok_scale, int64_t b, int64_t K, int64_t N,

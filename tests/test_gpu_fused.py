@@ -97,9 +97,23 @@ def test_gemv_ternary_fused_matches(tl, K, N, b):
     y_ref = tl.gemv_ternary(tl.hadamard_blk(x), packed, s_d, out_dtype=torch.float32)
     y_fus = tl.gemv_ternary_x(x, packed, s_d, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(y_fus.cpu().numpy(), y_ref.cpu().numpy())
+    _check_fused_vs_sequence(tl, y_fus.cpu().numpy(), y_ref.cpu().numpy())
     ref = oracle.gemv_ternary(oracle.rotate_exact(synth.bf16_bits_to_f32(xbits)), codes, scales)
     assert oracle.rel_fro(y_fus.cpu().numpy(), ref) <= REL_TOL
+
+
+def _check_fused_vs_sequence(tl, y_fus, y_seq):
+    """The prep + GEMV pair is bit-identical to the rotation kernel + GEMV; the
+    one-launch kernel (one or two tokens) scales its limbs per 1024-block instead
+    of per token, so it differs from them by the rounding of the limbs alone:
+    both lie within about 3e-5 of the exact layer."""
+    kname = tl.last_kernel_name()
+    if kname.startswith("gemv_rot"):
+        e = oracle.rel_fro(y_fus, y_seq)
+        announce(f"  one launch ({kname}): rel_fro vs rotation + GEMV = {e:.3e}")
+        assert e <= 2e-4
+    else:
+        np.testing.assert_array_equal(y_fus, y_seq)
 
 
 @pytest.mark.parametrize("T,K,signed", [(1, 1024, False), (7, 5120, True), (64, 17408, False),
@@ -138,11 +152,15 @@ def test_quant_fused_zero_token(tl):
                                           (17408, 5120, 1, True), (17408, 5120, 2, False),
                                           (5120, 34816, 1, False), (5120, 5120, 2, False),
                                           (1024, 300, 1, True), (3072, 77, 2, False),
-                                          (33792, 1024, 1, False)])
+                                          (33792, 1024, 1, False), (6144, 4100, 1, True),
+                                          (6144, 12288, 1, False), (2048, 6144, 2, True),
+                                          (5120, 12289, 1, False), (7168, 1000, 1, False)])
 def test_gemv_ternary_fused_signed_shapes(tl, K, N, b, signed):
     """Decode at b <= 2 from the raw input, with and without signs, on the layer
-    shapes and ragged ones: bit-identical to the rotation kernel + GEMV sequence
-    and within the relative bound of the oracle."""
+    shapes and ragged ones (the one-launch kernel with 16 and 32 rows per
+    workgroup, one to six blocks, and just past its limits in N and K): within the
+    relative bound of the oracle, and bit-identical to the rotation kernel + GEMV
+    sequence where the prep + GEMV pair runs."""
     import torch
     d = dev()
     announce(f"gemv_ternary_x signed-shapes K={K} N={N} b={b} signed={signed}")
@@ -159,7 +177,9 @@ def test_gemv_ternary_fused_signed_shapes(tl, K, N, b, signed):
     y_fus = torch.full((b, N), float("nan"), dtype=torch.float32, device=d)
     tl.gemv_ternary_x(x, packed, s_d, signs=signs, out=y_fus)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(y_fus.cpu().numpy(), y_ref.cpu().numpy())
+    _check_fused_vs_sequence(tl, y_fus.cpu().numpy(), y_ref.cpu().numpy())
     xr = oracle.rotate_exact(synth.bf16_bits_to_f32(xbits), sg)
     ref = oracle.gemv_ternary(xr, codes, scales)
-    assert oracle.rel_fro(y_fus.cpu().numpy(), ref) <= REL_TOL
+    e = oracle.rel_fro(y_fus.cpu().numpy(), ref)
+    announce(f"  kernel={tl.last_kernel_name()} rel_fro vs exact layer = {e:.3e}")
+    assert e <= REL_TOL

@@ -30,7 +30,8 @@ def _layer(tl, d, K, N, seed):
     return codes, scales, sd, packed, q, rs
 
 
-@pytest.mark.parametrize("T,K,N,signed", [(5, 1024, 300, False), (40, 2048, 1000, True), (64, 1024, 77, False),
+@pytest.mark.parametrize("T,K,N,signed", [(1, 5120, 1000, True), (2, 3072, 5000, False),
+                                          (5, 1024, 300, False), (40, 2048, 1000, True), (64, 1024, 77, False),
                                           (80, 1024, 300, True), (17, 1024, 20544, False), (200, 3072, 129, False)])
 def test_linear_apply(tl, T, K, N, signed):
     import torch
