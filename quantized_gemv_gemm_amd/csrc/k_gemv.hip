@@ -1219,11 +1219,11 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
   return hipGetLastError();
 }
 
-// The one-launch path pays for its redundant rotations (every workgroup rotates
-// every block of every token) with fewer launches and no limb round trip; it is
-// ahead while the workgroups are few: measured (device time, qkv-like K = 5120)
-// one token up to N = 10240 (9.1 against 11.0 us for prep + GEMV at N = 10240,
-// 6.7 against 9.6 at 5120, behind at 34816), two tokens up to N = 5120.
+// The one-launch path trades redundant rotations (every workgroup rotates every
+// block of every token) for one launch fewer and no limb round trip, so it is
+// ahead while the workgroups are few.  Measured (device time, K = 5120) against
+// prep + GEMV: one token 9.1 vs 11.0 us at N = 10240, 6.7 vs 9.6 at 5120, behind
+// at 34816; two tokens 9.6 vs 10.0 at N = 5120, behind at 10240.
 bool gemv_rot_supported(int64_t b, int64_t K, int64_t N) {
   if (K <= 0 || K % kHBlock || K / kHBlock > kRotMaxBlocks) return false;
   return (b == 1 && N <= 12288) || (b == 2 && N <= 6144);
