@@ -51,7 +51,7 @@
 // that the pieces or sub-tiles of one weight strip share an L2.
 // With fewer 128 x 256 tiles than compute units (few tokens, or a narrow output
 // with long K), the whole problem takes 128 x 128 tiles (each wave 128 x 32) on
-// the two-per-CU pipeline, split along K into as many pieces as fit 512 slots.
+// the two-per-CU pipeline, split along K into at most 6 pieces (512 slots).
 // No workgroup ever waits for another.
 #include <algorithm>
 
@@ -363,9 +363,9 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const flo
 // Left-over tiles are cut or split so that the last round is at most one
 // workgroup per CU.  Problems with fewer big tiles than CUs (few tokens, or a
 // narrow output with long K) take 128 x 128 tiles on the two-per-CU pipeline
-// instead, split along K into as many pieces as fill at most 512 slots: twice the
-// workgroups of the same size at no extra partial-tile bytes (S partial tiles of
-// half the size), each CU interleaving two of them.
+// instead, split along K into up to 6 pieces (at most 512 workgroups, S chosen by
+// a small cost model): twice the workgroups of the same size at no extra
+// partial-tile bytes (S partial tiles of half the size).
 inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   Schedule sc;
   sc.mb = int((M + kBM - 1) / kBM);
@@ -375,8 +375,17 @@ inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
     const int mmb = int((M + Mid::BM - 1) / Mid::BM);
     const int mtiles = mmb * int((N + Mid::BN - 1) / Mid::BN);
     if (mtiles <= 2 * kSlots) {
+      // S by a cost in pair-steps fitted to measurements: the longest piece
+      // (padded to an even pair count) at 0.9 per pair when every workgroup has
+      // a CU to itself, 2.0 when some CUs hold two, plus one per extra piece
+      // (its partial tile read back by the last piece); ties go to fewer pieces.
       int S = 1;
-      while (S < kMaxSplit && (S + 1) * mtiles <= 2 * kSlots && S + 1 <= GP) ++S;
+      double best = 1e30;
+      for (int s = 1; s <= kMaxSplit && s * mtiles <= 2 * kSlots && s <= GP; ++s) {
+        const int64_t piece = (GP + s - 1) / s;
+        const double cost = double(piece + (piece & 1)) * (s * mtiles > kSlots ? 2.0 : 0.9) + (s - 1);
+        if (cost < best - 1e-9) best = cost, S = s;
+      }
       sc.mid = 1;
       sc.two = 1;
       sc.round = 2 * kSlots;

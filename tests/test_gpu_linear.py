@@ -70,7 +70,7 @@ def test_linear_workspace_shared_across_paths(tl):
     touches the int8 GEMM's counters, which every call leaves at zero."""
     import torch
     d = dev()
-    K, N = 5120, 20544        # T = 17 takes the int8 path (split-K counters in use), T = 9 the GEMV
+    K, N = 17408, 6000        # T = 17 takes the int8 path (split-K counters in use), T = 9 the GEMV
     codes, scales, sd, packed, q, rs = _layer(tl, d, K, N, 5)
     ws = torch.zeros((max(tl.linear_workspace_size(17, K, N), tl.linear_workspace_size(9, K, N)),),
                      dtype=torch.uint8, device=d)

@@ -341,9 +341,10 @@ def test_gemm_two_per_cu_ragged(tl, M, K, N):
 @pytest.mark.parametrize("M,K,N", [(512, 17408, 5120), (130, 2048, 1000), (33, 384, 4000), (200, 640, 40),
                                    (64, 128, 700)])
 def test_gemm_mid_tiles(tl, M, K, N):
-    """Fewer 128 x 256 tiles than compute units: 128 x 128 tiles, two per CU, split
-    along K (down at 512 tokens: 160 tiles x 3 pieces; 16 tiles x 6; ragged M and
-    N; an odd group count; N narrower than a tile; one pair of groups, no split)."""
+    """Fewer 128 x 256 tiles than compute units: 128 x 128 tiles on the two-per-CU
+    pipeline, split along K or not (down at 512 tokens: 160 tiles x 3 pieces;
+    16 tiles x 2; ragged M and N; an odd group count; N narrower than a tile;
+    one pair of groups)."""
     d = dev()
     rng = np.random.default_rng(M + K + N + 7)
     codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
