@@ -306,7 +306,7 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
  *   [P1] "前提" (the layer), "4. 効いた高速化" (the prefill path); the choice by
  *   token count mirrors the page's decode / prefill split.
  * tl_linear_path: up to 16 tokens the GEMV; 17..64 tokens the GEMV while
- * ceil(T/16) * N * K <= 3 * 2^26 (every 16-token chunk streams all weights
+ * ceil(T/16) * N * K <= 2^27 (every 16-token chunk streams all weights
  * again), else the int8 path; above 64 tokens the int8 path.
  * The rule follows a measured token sweep of both paths at the qkv
  * (5120 -> 10240), gate_up (5120 -> 34816) and down (17408 -> 5120) shapes.

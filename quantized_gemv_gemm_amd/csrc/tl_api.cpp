@@ -360,11 +360,11 @@ int tl_linear_path(int64_t T, int64_t K, int64_t N) {
   if (T > tl::kGemvMaxTokens) return TL_PATH_INT8;
   // 17..64 tokens: the GEMV runs one chunk of 16 tokens per grid row, each
   // streaming all N x K weights again, while the int8 path's time hardly grows
-  // with T at this size; the GEMV stays ahead up to about 3 x 2^26 streamed
-  // weights (qkv 5120 x 10240: three chunks; down 17408 x 5120: two; gate_up
-  // 5120 x 34816: none beyond the first).
+  // with T at this size; the GEMV stays ahead up to about 2^27 streamed weights
+  // (qkv 5120 x 10240: two chunks; down 17408 x 5120 and gate_up 5120 x 34816:
+  // none beyond the first).
   const int64_t streamed = tl::limb_chunks(T) * N * K;
-  return streamed <= (int64_t(3) << 26) ? TL_PATH_GEMV : TL_PATH_INT8;
+  return streamed <= (int64_t(1) << 27) ? TL_PATH_GEMV : TL_PATH_INT8;
 }
 
 size_t tl_linear_workspace_size(int64_t T, int64_t K, int64_t N) {

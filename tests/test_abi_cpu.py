@@ -172,17 +172,16 @@ def test_fused_input_rejections():
 
 
 def test_linear_path_rule():
-    """Up to 16 tokens the GEMV; 17..64 while ceil(T/16) N K <= 3 * 2^26; above 64 the int8 path."""
+    """Up to 16 tokens the GEMV; 17..64 while ceil(T/16) N K <= 2^27; above 64 the int8 path."""
     P = tl.linear_path
     for T in (0, 1, 8, 16):
         assert P(T, 5120, 34816) == tl.PATH_GEMV and P(T, 17408, 1 << 20) == tl.PATH_GEMV
-    assert P(48, 5120, 10240) == tl.PATH_GEMV      # qkv: 3 chunks x 52.4e6 weights
-    assert P(49, 5120, 10240) == tl.PATH_INT8      # 4 chunks
-    assert P(32, 17408, 5120) == tl.PATH_GEMV      # down: 2 chunks x 89.1e6
-    assert P(33, 17408, 5120) == tl.PATH_INT8
+    assert P(32, 5120, 10240) == tl.PATH_GEMV      # qkv: 2 chunks x 52.4e6 weights
+    assert P(33, 5120, 10240) == tl.PATH_INT8      # 3 chunks
+    assert P(17, 17408, 5120) == tl.PATH_INT8      # down: 2 chunks x 89.1e6
     assert P(17, 5120, 34816) == tl.PATH_INT8      # gate_up: 2 chunks x 178e6
-    assert P(17, 1024, 98304) == tl.PATH_GEMV      # exactly 3 * 2^26 streamed weights
-    assert P(17, 1024, 98305) == tl.PATH_INT8
+    assert P(17, 1024, 65536) == tl.PATH_GEMV      # exactly 2^27 streamed weights
+    assert P(17, 1024, 65537) == tl.PATH_INT8
     assert P(65, 1024, 64) == tl.PATH_INT8 and P(512, 5120, 10240) == tl.PATH_INT8
 
 def test_linear_rejections():
