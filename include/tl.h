@@ -283,9 +283,9 @@ int tl_quant_act_int8_x(const uint16_t *x, int64_t T, int64_t K, const int8_t *s
  *                across shapes, without clearing.  Calls that overlap in time
  *                must not share one.
  * The size depends only on (M, K, N): the schedule is fixed for the 256
- * compute units of gfx950 (whole rounds of 128 x 256 tiles, the left-over
- * tiles split along K or cut into sub-tiles; with fewer 128 x 256 tiles than
- * compute units, 128 x 128 tiles split along K into up to 6 pieces).
+ * compute units of gfx950 (whole rounds of 512 tiles, two per compute unit,
+ * of 128 x 256 or, with fewer than 512 such tiles, of 128 x 128; the left-over
+ * tiles split along K into up to 6 pieces or cut into sub-tiles).
  * Requires K > 0, K % 128 == 0, K <= 133120.
  */
 size_t tl_gemm_workspace_size(int64_t M, int64_t K, int64_t N);

@@ -49,9 +49,9 @@
 //    independent).
 // The left-over work is dealt out XCD by XCD (workgroup i runs on XCD i % 8), so
 // that the pieces or sub-tiles of one weight strip share an L2.
-// With fewer 128 x 256 tiles than compute units (few tokens, or a narrow output
-// with long K), the whole problem takes 128 x 128 tiles (each wave 128 x 32) on
-// the two-per-CU pipeline, split along K into at most 6 pieces (512 slots).
+// With fewer than 512 tiles of 128 x 256 (fewer than two per compute unit), the
+// problem takes 128 x 128 tiles (each wave 128 x 32) on the two-per-CU pipeline
+// instead: whole rounds of 512, the rest split along K into at most 6 pieces.
 // No workgroup ever waits for another.
 #include <algorithm>
 
@@ -358,44 +358,43 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const flo
   }
 }
 
-// The two-per-CU pipeline runs when there are at least two tiles per compute unit
-// (whole rounds of 512); otherwise one deeper-pipelined workgroup per CU.
-// Left-over tiles are cut or split so that the last round is at most one
-// workgroup per CU.  Problems with fewer big tiles than CUs (few tokens, or a
-// narrow output with long K) take 128 x 128 tiles on the two-per-CU pipeline
-// instead, split along K into up to 6 pieces (at most 512 workgroups, S chosen by
-// a small cost model): twice the workgroups of the same size at no extra
-// partial-tile bytes (S partial tiles of half the size).
+// With at least 512 tiles of 128 x 256 (two per compute unit) the big tiles run
+// in whole rounds of 512 and the left-over tiles are cut or split so that the
+// last round is at most one workgroup per CU.  With fewer, the problem takes
+// 128 x 128 tiles instead, also two per CU: twice the workgroups, and, when the
+// left-over ones are split along K, S partial tiles of half the size.
 inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
   Schedule sc;
   sc.mb = int((M + kBM - 1) / kBM);
   sc.tiles = sc.mb * int((N + kBN - 1) / kBN);
   sc.mid = 0;
-  if (sc.tiles < kSlots) {
+  if (sc.tiles < 2 * kSlots) {
+    // Mid tiles: whole rounds of 512 workgroups (two per CU), the rest split
+    // along K into S pieces (S x rest <= 512).  S by a cost in pair-steps fitted
+    // to measurements: the longest piece (padded to an even pair count) at 0.9
+    // per pair when every workgroup has a CU to itself, 2.0 when some CUs hold
+    // two, plus one per extra piece (its partial tile read back by the last
+    // piece); ties go to fewer pieces.
     const int mmb = int((M + Mid::BM - 1) / Mid::BM);
     const int mtiles = mmb * int((N + Mid::BN - 1) / Mid::BN);
-    if (mtiles <= 2 * kSlots) {
-      // S by a cost in pair-steps fitted to measurements: the longest piece
-      // (padded to an even pair count) at 0.9 per pair when every workgroup has
-      // a CU to itself, 2.0 when some CUs hold two, plus one per extra piece
-      // (its partial tile read back by the last piece); ties go to fewer pieces.
-      int S = 1;
-      double best = 1e30;
-      for (int s = 1; s <= kMaxSplit && s * mtiles <= 2 * kSlots && s <= GP; ++s) {
-        const int64_t piece = (GP + s - 1) / s;
-        const double cost = double(piece + (piece & 1)) * (s * mtiles > kSlots ? 2.0 : 0.9) + (s - 1);
-        if (cost < best - 1e-9) best = cost, S = s;
-      }
-      sc.mid = 1;
-      sc.two = 1;
-      sc.round = 2 * kSlots;
-      sc.mb = mmb;
-      sc.tiles = mtiles;
-      sc.full = 0;
-      sc.split = S;
-      sc.narrow = 0;
-      return sc;
+    const int full = mtiles / (2 * kSlots) * (2 * kSlots);
+    const int left = mtiles - full;
+    int S = 1;
+    double best = 1e30;
+    for (int s = 1; left && s <= kMaxSplit && s * left <= 2 * kSlots && s <= GP; ++s) {
+      const int64_t piece = (GP + s - 1) / s;
+      const double cost = double(piece + (piece & 1)) * (s * left > kSlots ? 2.0 : 0.9) + (s - 1);
+      if (cost < best - 1e-9) best = cost, S = s;
     }
+    sc.mid = 1;
+    sc.two = 1;
+    sc.round = 2 * kSlots;
+    sc.mb = mmb;
+    sc.tiles = mtiles;
+    sc.split = S;
+    sc.full = S > 1 ? full : mtiles;
+    sc.narrow = 0;
+    return sc;
   }
   sc.two = sc.tiles >= 2 * kSlots;
   sc.round = sc.two ? 2 * kSlots : kSlots;
@@ -726,12 +725,22 @@ __global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
   const int g = blockIdx.x;
   if constexpr (TWO) {
     if (sc.mid) {
-      // Mid tile e / S, K piece e % S (no piece when S = 1)
-      const int e = xcd_item(g, int(sc.grid()));
-      const int S = sc.split;
-      const int tile = e / S, piece = S > 1 ? e % S : -1;
-      const int k0 = S > 1 ? int(int64_t(GP) * piece / S) : 0;
-      const int k1 = S > 1 ? int(int64_t(GP) * (piece + 1) / S) : GP;
+      int tile, piece = -1, e = 0, k0 = 0, k1 = GP;
+      if (g < sc.full) {
+        // whole Mid tiles in rounds, the M-blocks of a strip on one XCD
+        const int round = g / sc.round, u = g % sc.round;
+        tile = (sc.round % kXcds == 0 && sc.full - round * sc.round >= sc.round)
+                   ? round * sc.round + (sc.round / kXcds) * (u % kXcds) + u / kXcds
+                   : g;
+      } else {
+        // left-over Mid tile full + e / S, K piece e % S (no piece when S = 1)
+        e = xcd_item(g - sc.full, int(sc.grid() - sc.full));
+        const int S = sc.split;
+        tile = sc.full + e / S;
+        piece = S > 1 ? e % S : -1;
+        k0 = S > 1 ? int(int64_t(GP) * piece / S) : 0;
+        k1 = S > 1 ? int(int64_t(GP) * (piece + 1) / S) : GP;
+      }
       const int64_t m0 = int64_t(tile % sc.mb) * Mid::BM;
       const int64_t n0 = int64_t(tile / sc.mb) * Mid::BN;
       run_tile<Mid::BM / 32, Mid::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);

@@ -307,10 +307,11 @@ def test_gemm_ragged(tl, M, K, N):
     _gemm_check(tl, codes, scales, packed, q, rs, xq, sx, "ragged")
 
 
-@pytest.mark.parametrize("M,K,N", [(300, 256, 22940), (130, 384, 32800)])
+@pytest.mark.parametrize("M,K,N", [(500, 256, 33500), (130, 384, 65700)])
 def test_gemm_narrow_tail(tl, M, K, N):
-    """A short last round cut into 32 x 128 sub-tiles, some of them partly or wholly
-    past M and N (300 rows = 2 whole M-blocks + 44 rows; a ragged last strip)."""
+    """A short last round (524 or 514 tiles of 128 x 256) cut into 32 x 128
+    sub-tiles, some of them partly or wholly past M and N (500 rows = 3 whole
+    M-blocks + 116 rows; 130 = 1 + 2 rows; ragged last strips)."""
     d = dev()
     rng = np.random.default_rng(M + K + N)
     codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
@@ -339,12 +340,12 @@ def test_gemm_two_per_cu_ragged(tl, M, K, N):
 
 
 @pytest.mark.parametrize("M,K,N", [(512, 17408, 5120), (130, 2048, 1000), (33, 384, 4000), (200, 640, 40),
-                                   (64, 128, 700)])
+                                   (64, 128, 700), (1500, 640, 6000), (300, 256, 22940)])
 def test_gemm_mid_tiles(tl, M, K, N):
-    """Fewer 128 x 256 tiles than compute units: 128 x 128 tiles on the two-per-CU
-    pipeline, split along K or not (down at 512 tokens: 160 tiles x 3 pieces;
-    16 tiles x 2; ragged M and N; an odd group count; N narrower than a tile;
-    one pair of groups)."""
+    """Fewer than 512 tiles of 128 x 256: 128 x 128 tiles on the two-per-CU
+    pipeline (down at 512 tokens: 160 tiles x 3 pieces; 16 tiles x 2; ragged M and
+    N; an odd group count; N narrower than a tile; one pair of groups; a whole
+    round of 512 and 52 left-over tiles x 2 pieces; 540 tiles, no split)."""
     d = dev()
     rng = np.random.default_rng(M + K + N + 7)
     codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
