@@ -13,31 +13,24 @@
 // 128 int32 accumulators per lane), so every expanded weight fragment feeds four
 // MFMAs.  The K loop steps one pair of 128-wide scale groups (8 MFMA k-steps).
 //
-// Two pipelines.  With at least two tiles per compute unit (512 or more), two
-// workgroups share each CU (256 registers per lane each), so that one's stalls
-// are covered by the other's MFMAs:
+// Pipeline: two workgroups share each compute unit (256 registers per lane
+// each), so that one's stalls are covered by the other's MFMAs:
 //  * the activation tile of pair p+1 is loaded straight into the second of two
 //    LDS buffers (buffer loads with the LDS destination, 1 KB per instruction)
 //    while pair p is computed from the first; rows are unpadded and each 16-byte
 //    chunk c of row r sits at c ^ (r % 16), so the fragment reads of 16 rows
 //    hit 16 different bank groups; the reads are issued by hand with their own
 //    waits (the compiler would otherwise wait for every load before them);
-//  * packed weight words arrive in a two-deep register ring.
-// Otherwise one workgroup per CU with a deeper pipeline:
-//  * the activation tile of pair p sits in one of three LDS buffers; the one of
-//    pair p+1 is already complete, the one of pair p+2 is written half way
-//    through pair p from registers loaded one pair earlier;
-//  * packed weight words arrive in a four-deep register ring.
-// In both, weight words are loaded straight from the 1 KB packed tiles (two
-// 16-byte loads per column per pair), the LDS reads and the weight expansion of
-// k-step s+1 are issued between the MFMAs of k-step s, and there is one barrier
-// per pair.
+//  * packed weight words arrive in a two-deep register ring, loaded straight
+//    from the 1 KB packed tiles (two 16-byte loads per column per pair);
+//  * the LDS reads and the weight expansion of k-step s+1 are issued between the
+//    MFMAs of k-step s, and there is one barrier per pair.
 // The expansion code -> code*q is one v_perm_b32 per 4 weights: the selector
 // bytes are the 2-bit fields ((w >> 2r) & 0x03030303) and the table holds
 // {0, q, -, -q}.
 //
-// Work distribution: the tiles are dealt out in whole rounds of workgroups (one
-// or two per compute unit), each round XCD-aware so that the M-blocks of a
+// Work distribution: the tiles are dealt out in whole rounds of workgroups (two
+// per compute unit), each round XCD-aware so that the M-blocks of a
 // weight strip run on one XCD and share its L2.  The tiles left over for a last,
 // partial round are either
 //  * cut into eight 32 x 128 sub-tiles (when at most 256 / 8 are left), each a
@@ -66,7 +59,6 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kPairK = 2 * kGroup;        // k per pipeline stage: one pair of groups
-constexpr int kAStride = kPairK + 16;     // LDS row pitch in bytes (padding spreads banks)
 constexpr int kSlots = 256;               // the compute units of gfx950
 constexpr int kXcds = 8;                  // workgroup i runs on XCD i % 8
 constexpr int kMaxSplit = 6;
@@ -76,29 +68,23 @@ constexpr int kMaxSplit = 6;
 template <int MT, int J>
 struct Tile {
   static constexpr int BM = 32 * MT, BN = 4 * 32 * J;
-  static constexpr int ABuf = BM * kAStride;  // one activation stage in LDS
-  static constexpr int APieces = 2 * MT;      // 16-byte activation pieces per thread and pair
   static constexpr int Ints = BM * BN;
-  static_assert(BM * kPairK == kThreads * APieces * 16, "A stage = APieces x 16 bytes per thread");
 };
 typedef Tile<4, 2> Big;     // 128 x 256: the tile of the whole rounds
 typedef Tile<1, 1> Narrow;  // 32 x 128: an eighth of a big tile, for a short last round
 typedef Tile<4, 1> Mid;     // 128 x 128: the tile of problems with fewer big tiles than CUs
 constexpr int kBM = Big::BM;
 constexpr int kBN = Big::BN;
-constexpr int kABuf = Big::ABuf;
 constexpr int kTileInts = Big::Ints;
 constexpr int kNarrowPerTile = (Big::BM / Narrow::BM) * (Big::BN / Narrow::BN);
-// Two pipelines (TWO selects): one workgroup per compute unit with three padded
-// activation stages in LDS staged through registers and a four-deep weight ring;
-// or two workgroups per compute unit (256 registers per lane each) with two
-// swizzled activation stages loaded straight into LDS and a two-deep weight ring.
-template <bool TWO>
-struct Pipe {
-  static constexpr int lds = (TWO ? 2 : 3) * kABuf;  // activation stages; also the epilogue staging room
-  static constexpr int per_cu = TWO ? 2 : 1;
-  static constexpr int turn = TWO ? 2 : 4;           // pairs per ring turn (the K loop pads to it)
-};
+// Two workgroups per compute unit (256 registers per lane each): two activation
+// stages of 128 rows x 256 bytes loaded straight into LDS, weights in a two-deep
+// register ring, the K loop in turns of two pairs.  The LDS block also serves as
+// the epilogue's staging room (128 rows of 256 bf16 values and a 16-byte pad per
+// row, written in one pass).
+constexpr int kStageLds = 2 * kBM * (kPairK + 16);
+constexpr int kWgPerCu = 2;
+constexpr int kTurn = 2;  // pairs per ring turn (the K loop pads to it)
 
 static_assert(kTileInts == kThreads * 128, "128 accumulators per thread");
 
@@ -112,8 +98,7 @@ struct BStage {
 struct Schedule {
   int mb;         // M-blocks
   int tiles;      // MB * N-strips
-  int two;        // 1: the two-workgroups-per-CU pipeline
-  int round;      // workgroups per whole round: kSlots times workgroups per CU
+  int round;      // workgroups per whole round: two per compute unit
   int full;       // tiles computed whole, in whole rounds (the rest are split or cut)
   int split;      // pieces per left-over tile along K (1: nothing is split)
   int narrow;     // 1: the left-over tiles are cut into kNarrowPerTile sub-tiles
@@ -144,9 +129,6 @@ __device__ __forceinline__ v4i expand_word(uint32_t w, uint32_t table) {
 template <int J>
 struct Frame {
   __amdgpu_buffer_rsrc_t ra, rb, rq;
-  int aoff;       // byte offset of this thread's first staged activation piece
-  int astep;      // 16 rows of activations, in bytes
-  int adst;       // LDS offset of the first piece; piece i is 16 rows further
   int boff[J];    // this lane's 16 bytes of the first tile of its weight column, per N tile
   int qoff[J];    // q row of that column
   int G;
@@ -154,15 +136,6 @@ struct Frame {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9)
 constexpr int kCoherent = 16;           // cache policy sc1: coherent across the XCDs' L2s
-
-// The row of every access is in the per-lane (VGPR) offset, which the buffer range
-// check covers; the scalar offset only moves along the row (p * 256 < K).
-template <int NP, int J>
-__device__ __forceinline__ void load_a(v4u (&a)[NP], const Frame<J> &f, int p) {
-#pragma unroll
-  for (int i = 0; i < NP; ++i)
-    a[i] = __builtin_amdgcn_raw_buffer_load_b128(f.ra, f.aoff + i * f.astep, p * kPairK, 0);
-}
 
 template <int J>
 __device__ __forceinline__ void load_b(BStage<J> &b, const Frame<J> &f, int p, bool live) {
@@ -180,22 +153,9 @@ __device__ __forceinline__ void load_b(BStage<J> &b, const Frame<J> &f, int p, b
   b.keep[1] = live && 2 * p + 1 < f.G ? ~0u : 0u;
 }
 
-template <int NP, int J>
-__device__ __forceinline__ void store_a(int8_t *buf, const v4u (&a)[NP], const Frame<J> &f) {
-#pragma unroll
-  for (int i = 0; i < NP; ++i) *reinterpret_cast<v4u *>(buf + f.adst + 16 * kAStride * i) = a[i];
-}
-
 // k-step s (0..7) of a pair: group gi = s / 4, sub-step ss = s % 4.  Word 4h + ss
 // of the lane's column in group gi: words 4h, 4h+1 sit in the lane-quarter 2h slot
 // of the tile, 4h+2, 4h+3 in the 2h+1 slot.
-template <int MT>
-__device__ __forceinline__ void fetch_a(v4i (&af)[MT], const int8_t *abase, int s) {
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    af[mt] = *reinterpret_cast<const v4i *>(abase + 32 * mt * kAStride + kGroup * (s >> 2) + 16 * (s & 3));
-}
-
 template <int J>
 __device__ __forceinline__ void fetch_b(v4i (&bf)[J], const BStage<J> &b, int s) {
   const int gi = s >> 2, ss = s & 3;
@@ -213,58 +173,6 @@ __device__ __forceinline__ void mfma_step(const v4i (&af)[MT], const v4i (&bf)[J
       acc[mt][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[mt], bf[j], acc[mt][j], 0, 0, 0);
 }
 
-// One pair p.  Weight ring slot S = (p - p0) mod 4 is fixed at compile time; the
-// LDS buffer lb = (p - p0) mod 3 is a run-time offset.  On entry af[0] / bf[0]
-// hold k-step 0 of pair p, the LDS buffer of pair p+1 is complete, anext[S & 1]
-// holds (or is loading) the activation stage of pair p+2 and anext[~S & 1] that
-// of p+3, and the ring holds (or is loading) pairs p+1..p+3.  On exit the same
-// holds for p+1.  Pairs before k0 are padding
-// (zero weights), data indices are clamped into [k0, k1).
-template <int S, int MT, int J>
-__device__ __forceinline__ void pair_body(int p, int k0, int plast, int &lb, const Frame<J> &f,
-                                          int8_t *lds, const int8_t *aread, BStage<J> (&ring)[4],
-                                          v4u (&anext)[2][Tile<MT, J>::APieces], v4i (&af)[2][MT],
-                                          v4i (&bf)[2][J], v16i (&acc)[MT][J]) {
-  constexpr int S1 = (S + 1) % 4;
-  constexpr int AB = Tile<MT, J>::ABuf;
-  const int lb1 = lb == 2 ? 0 : lb + 1, lb2 = lb1 == 2 ? 0 : lb1 + 1;
-  const int8_t *cur = aread + lb * AB;
-  const int8_t *nxt = aread + lb1 * AB;
-  // Scheduling fences keep the issue order: LDS reads for k-step s+1, then the
-  // MFMAs of k-step s interleaved with the expansion for s+1, then stage traffic.
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (s < 7)
-      fetch_a(af[(s + 1) & 1], cur, s + 1);
-    else
-      fetch_a(af[0], nxt, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(af[s & 1], bf[s & 1], acc);
-    if (s < 7)
-      fetch_b(bf[(s + 1) & 1], ring[S], s + 1);
-    else
-      fetch_b(bf[0], ring[S1], 0);
-#pragma unroll
-    for (int i = 0; i < MT * J; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (s == 3) {
-      store_a(lds + lb2 * AB, anext[S & 1], f);
-      load_a(anext[S & 1], f, min(max(p + 4, k0), plast));
-    }
-    if (s == 7) load_b(ring[S], f, min(max(p + 4, k0), plast), p + 4 >= k0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  lb = lb1;
-  __syncthreads();
-}
-
-// Tiles are dealt out in whole rounds of kSlots; the tiles left over for a last,
-// partial round are split into S pieces along K when that shortens the round.
-// Cost of a piece in pair-steps: its pairs rounded up to the ring turn of 4, plus
-// about one pair-step per partial tile the last piece has to add (128 KB each).
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // y = fl32(fl32(acc) * row_scale[n]) * tok_scale[m].  The lane holds column l32 of
@@ -387,7 +295,6 @@ inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
       if (cost < best - 1e-9) best = cost, S = s;
     }
     sc.mid = 1;
-    sc.two = 1;
     sc.round = 2 * kSlots;
     sc.mb = mmb;
     sc.tiles = mtiles;
@@ -396,9 +303,8 @@ inline Schedule make_schedule(int64_t M, int64_t N, int64_t GP) {
     sc.narrow = 0;
     return sc;
   }
-  sc.two = sc.tiles >= 2 * kSlots;
-  sc.round = sc.two ? 2 * kSlots : kSlots;
-  const int turn = sc.two ? Pipe<true>::turn : Pipe<false>::turn;
+  sc.round = 2 * kSlots;
+  const int turn = kTurn;
   sc.narrow = 0;
   const int left = sc.tiles % sc.round;
   int best = 1;
@@ -520,7 +426,7 @@ __device__ __forceinline__ void pair_body2(int p, int k0, int plast, const Frame
 // One workgroup tile of 32 MT x 128 J at (m0, n0) over the pairs [k0, k1).  A
 // piece of a K-split tile (piece >= 0, big tiles only) publishes its partial
 // tile and only the last piece to arrive runs the epilogue.
-template <int MT, int J, bool TWO>
+template <int MT, int J>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, int8_t *sA, float *s_tok,
                                          int *s_last, int64_t m0, int64_t n0, int k0, int k1, int tile,
                                          int piece, int slot) {
@@ -546,10 +452,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
     f.rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(a.q + n0 * G), (short)0, int(cols * G),
                                              kRsrcWord3);
   }
-  // activation staging: chunk c = tid + 256 i -> row c/16 = tid/16 + 16 i, 16-byte column tid%16
-  f.aoff = int((tid >> 4) * K) + 16 * (tid & 15);
-  f.astep = int(16 * K);
-  f.adst = (tid >> 4) * kAStride + 16 * (tid & 15);
   // token scales of the tile's rows (LDS, read in the epilogue) and this lane's row scales
   if (tid < T::BM) s_tok[tid] = a.tok_scale[m0 + tid < M ? m0 + tid : M - 1];
   float rsv[J];
@@ -571,62 +473,28 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][j][r] = 0;
 
-  if constexpr (TWO) {
-    // two LDS stages filled straight from memory, two weight slots; an even pair
-    // count (a leading zero-weight pair when odd)
-    const int p0 = k0 - ((k1 - k0) & 1);
-    const int plast = k1 - 1;
-    BStage<J> ring[2];
-    load_b(ring[0], f, min(max(p0, k0), plast), p0 >= k0);
-    load_b(ring[1], f, min(max(p0 + 1, k0), plast), p0 + 1 >= k0);
-    // DMA source offset of this lane: row 4 wave + lane / 16 (+ 16 i), logical chunk
-    const int rbase = 4 * wave + (lane >> 4);
-    const int dvoff = int(rbase * K) + 16 * ((lane & 15) ^ (rbase & 15));
-    dma_a2<MT, J>(f, sA, min(max(p0, k0), plast), wave, dvoff, K);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    const uint32_t rowaddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t *)sA + 256 * l32;
-    const int xsw = l32 & 15;
-    v4i af[2][MT], bf[2][J];
-    fetch_b(bf[0], ring[0], 0);
-    for (int p = p0; p < k1; p += 2) {
-      pair_body2<0, MT, J>(p, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
-      pair_body2<1, MT, J>(p + 1, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
-  } else {
-  // The pair count is padded up to a multiple of 4 with leading zero-weight
-  // pairs, so that the loop below only exits after a whole ring turn.
-  // prologue: LDS buffers 0 and 1 <- pairs p0, p0+1; registers <- pair p0+2;
-  // weight ring <- pairs p0 .. p0+3.  Indices are clamped into [k0, k1) (valid
-  // memory; a clamped copy is either padding or never used).
+  // two LDS stages filled straight from memory, two weight slots; an even pair
+  // count (a leading zero-weight pair when odd)
+  const int p0 = k0 - ((k1 - k0) & 1);
   const int plast = k1 - 1;
-  const int p0 = k0 - ((4 - (k1 - k0) % 4) % 4);
-  BStage<J> ring[4];
-  v4u anext[2][T::APieces];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) load_b(ring[i], f, min(max(p0 + i, k0), plast), p0 + i >= k0);
-  load_a(anext[0], f, k0);
-  load_a(anext[1], f, min(max(p0 + 1, k0), plast));
-  store_a(sA, anext[0], f);
-  load_a(anext[0], f, min(max(p0 + 2, k0), plast));
-  store_a(sA + T::ABuf, anext[1], f);
-  load_a(anext[1], f, min(max(p0 + 3, k0), plast));
+  BStage<J> ring[2];
+  load_b(ring[0], f, min(max(p0, k0), plast), p0 >= k0);
+  load_b(ring[1], f, min(max(p0 + 1, k0), plast), p0 + 1 >= k0);
+  // DMA source offset of this lane: row 4 wave + lane / 16 (+ 16 i), logical chunk
+  const int rbase = 4 * wave + (lane >> 4);
+  const int dvoff = int(rbase * K) + 16 * ((lane & 15) ^ (rbase & 15));
+  dma_a2<MT, J>(f, sA, min(max(p0, k0), plast), wave, dvoff, K);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-
-  const int8_t *aread = sA + l32 * kAStride + 64 * h;
+  const uint32_t rowaddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t *)sA + 256 * l32;
+  const int xsw = l32 & 15;
   v4i af[2][MT], bf[2][J];
-  fetch_a(af[0], aread, 0);
   fetch_b(bf[0], ring[0], 0);
-
-  int lb = 0;
-  for (int p = p0; p < k1; p += 4) {
-    pair_body<0, MT, J>(p, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-    pair_body<1, MT, J>(p + 1, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-    pair_body<2, MT, J>(p + 2, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
-    pair_body<3, MT, J>(p + 3, k0, plast, lb, f, sA, aread, ring, anext, af, bf, acc);
+  for (int p = p0; p < k1; p += 2) {
+    pair_body2<0, MT, J>(p, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
+    pair_body2<1, MT, J>(p + 1, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
   }
-  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
 
   if (piece >= 0) {
     // Split tile: publish this piece, and only the last piece to arrive goes on.
@@ -679,8 +547,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
 
   const bool whole = m0 + T::BM <= M && n0 + T::BN <= N;
   if (whole && !a.acc_out && N % 8 == 0) {  // rows of y start on 16-byte boundaries
-    if (a.y_dtype == TL_F32) epilogue_lds<true, MT, J, Pipe<TWO>::lds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
-    else epilogue_lds<false, MT, J, Pipe<TWO>::lds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
+    if (a.y_dtype == TL_F32) epilogue_lds<true, MT, J, kStageLds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
+    else epilogue_lds<false, MT, J, kStageLds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
     return;
   }
   // variants with and without the exact accumulators, so that no store sits
@@ -708,14 +576,13 @@ __device__ __forceinline__ int xcd_item(int e, int total) {
   return (total / kXcds) * (e % kXcds) + e / kXcds;
 }
 
-template <bool TWO>
-__global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
+__global__ __launch_bounds__(kThreads, kWgPerCu) void gemm_i8_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int64_t M, int64_t K,
     int64_t N, const uint32_t *__restrict__ packed, const int8_t *__restrict__ q,
     const float *__restrict__ row_scale, void *__restrict__ y, int y_dtype,
     int32_t *__restrict__ acc_out, int32_t *__restrict__ part, int32_t *__restrict__ counters,
     Schedule sc) {
-  __shared__ __attribute__((aligned(16))) int8_t sA[Pipe<TWO>::lds];
+  __shared__ __attribute__((aligned(16))) int8_t sA[kStageLds];
   __shared__ __attribute__((aligned(16))) float s_tok[kBM];
   __shared__ int s_last;
   const GemmArgs a{xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters};
@@ -723,29 +590,27 @@ __global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
 
   // which tile and which K range this workgroup computes
   const int g = blockIdx.x;
-  if constexpr (TWO) {
-    if (sc.mid) {
-      int tile, piece = -1, e = 0, k0 = 0, k1 = GP;
-      if (g < sc.full) {
-        // whole Mid tiles in rounds, the M-blocks of a strip on one XCD
-        const int round = g / sc.round, u = g % sc.round;
-        tile = (sc.round % kXcds == 0 && sc.full - round * sc.round >= sc.round)
-                   ? round * sc.round + (sc.round / kXcds) * (u % kXcds) + u / kXcds
-                   : g;
-      } else {
-        // left-over Mid tile full + e / S, K piece e % S (no piece when S = 1)
-        e = xcd_item(g - sc.full, int(sc.grid() - sc.full));
-        const int S = sc.split;
-        tile = sc.full + e / S;
-        piece = S > 1 ? e % S : -1;
-        k0 = S > 1 ? int(int64_t(GP) * piece / S) : 0;
-        k1 = S > 1 ? int(int64_t(GP) * (piece + 1) / S) : GP;
-      }
-      const int64_t m0 = int64_t(tile % sc.mb) * Mid::BM;
-      const int64_t n0 = int64_t(tile / sc.mb) * Mid::BN;
-      run_tile<Mid::BM / 32, Mid::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);
-      return;
+  if (sc.mid) {
+    int tile, piece = -1, e = 0, k0 = 0, k1 = GP;
+    if (g < sc.full) {
+      // whole Mid tiles in rounds, the M-blocks of a strip on one XCD
+      const int round = g / sc.round, u = g % sc.round;
+      tile = (sc.round % kXcds == 0 && sc.full - round * sc.round >= sc.round)
+                 ? round * sc.round + (sc.round / kXcds) * (u % kXcds) + u / kXcds
+                 : g;
+    } else {
+      // left-over Mid tile full + e / S, K piece e % S (no piece when S = 1)
+      e = xcd_item(g - sc.full, int(sc.grid() - sc.full));
+      const int S = sc.split;
+      tile = sc.full + e / S;
+      piece = S > 1 ? e % S : -1;
+      k0 = S > 1 ? int(int64_t(GP) * piece / S) : 0;
+      k1 = S > 1 ? int(int64_t(GP) * (piece + 1) / S) : GP;
     }
+    const int64_t m0 = int64_t(tile % sc.mb) * Mid::BM;
+    const int64_t n0 = int64_t(tile / sc.mb) * Mid::BN;
+    run_tile<Mid::BM / 32, Mid::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);
+    return;
   }
   if (g >= sc.full && sc.narrow) {
     // sub-tile u of a left-over tile: rows 32 (u % 4), columns 128 (u / 4) of it
@@ -755,7 +620,7 @@ __global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
     const int64_t m0 = int64_t(tile % sc.mb) * kBM + Narrow::BM * (u % kRowCuts);
     const int64_t n0 = int64_t(tile / sc.mb) * kBN + Narrow::BN * (u / kRowCuts);
     if (m0 >= M || n0 >= N) return;  // the whole sub-tile lies past the output
-    run_tile<Narrow::BM / 32, Narrow::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
+    run_tile<Narrow::BM / 32, Narrow::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
     return;
   }
   int tile, piece = -1, slot = 0, k0 = 0, k1 = GP;
@@ -773,7 +638,7 @@ __global__ __launch_bounds__(kThreads, Pipe<TWO>::per_cu) void gemm_i8_kernel(
   }
   const int64_t m0 = int64_t(tile % sc.mb) * kBM;
   const int64_t n0 = int64_t(tile / sc.mb) * kBN;
-  run_tile<Big::BM / 32, Big::BN / 128, TWO>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
+  run_tile<Big::BM / 32, Big::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
 }
 
 // Workspace layout, the same for every shape so that one workspace serves calls
@@ -802,19 +667,14 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
     part = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
   }
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  if (s.two)
-    hipLaunchKernelGGL(gemm_i8_kernel<true>, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
-                       M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
-  else
-    hipLaunchKernelGGL(gemm_i8_kernel<false>, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
-                       M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
-  static const char *names[2][3] = {
-      {"gemm_i8_mfma32_128x256", "gemm_i8_mfma32_128x256_splitk", "gemm_i8_mfma32_128x256_narrowtail"},
-      {"gemm_i8_mfma32_128x256_lds2", "gemm_i8_mfma32_128x256_lds2_splitk", "gemm_i8_mfma32_128x256_lds2_narrowtail"}};
+  hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale, M, K,
+                     N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
+  static const char *names[3] = {"gemm_i8_mfma32_128x256_lds2", "gemm_i8_mfma32_128x256_lds2_splitk",
+                                  "gemm_i8_mfma32_128x256_lds2_narrowtail"};
   if (s.mid)
     set_last_kernel(s.split > 1 ? "gemm_i8_mfma32_128x128_lds2_splitk" : "gemm_i8_mfma32_128x128_lds2");
   else
-    set_last_kernel(names[s.two][s.narrow ? 2 : s.split > 1 ? 1 : 0]);
+    set_last_kernel(names[s.narrow ? 2 : s.split > 1 ? 1 : 0]);
   return hipGetLastError();
 }
 
