@@ -18,7 +18,8 @@
  *   - Every tensor argument is a DEVICE pointer owned by the caller, dense and
  *     row-major (C order).  The library allocates no device memory; scratch, when
  *     a call needs it, is a caller-provided workspace whose size a *_workspace_size
- *     query returns.
+ *     query returns (tl_linear_apply_noalloc instead uses a static device array
+ *     of tl_noalloc_scratch_bytes() per GPU, see there).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *     work is enqueued on it; no call synchronises.  A device fault surfaces at the
  *     caller's next synchronisation.
@@ -72,6 +73,7 @@ extern "C" {
 #define TL_ERR_UNSUPPORTED 6 /* no kernel variant for this request */
 #define TL_ERR_WORKSPACE 7   /* workspace missing or smaller than the query says */
 #define TL_ERR_ALIAS 8       /* an output overlaps an input or another output */
+#define TL_ERR_SCRATCH 9     /* beyond the static scratch of tl_linear_apply_noalloc */
 
 /* output element types */
 #define TL_BF16 0 /* bfloat16, round to nearest even from fp32 */
@@ -329,6 +331,27 @@ int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const in
                     const uint32_t *packed, const uint16_t *scales, const int8_t *q,
                     const float *row_scale, void *y, int y_dtype, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * tl_linear_apply_noalloc -- tl_linear_apply without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it.
+ * It runs the same kernels as tl_linear_apply (same path rule, same outputs, bit
+ * for bit) with the workspace taken from a static device array of
+ * tl_noalloc_scratch_bytes() bytes, one per GPU, held until the process ends.
+ * The first call on a device looks the array up and zeroes its counter region
+ * (one small kernel on `stream`); later calls leave the counters at zero as
+ * tl_linear_apply does.  Every call on one GPU shares that GPU's array: calls
+ * that overlap in time on one GPU (two streams, two host threads) race and must
+ * be serialised by the caller.  A request whose workspace
+ * (tl_linear_workspace_size(T, K, N)) exceeds the array returns TL_ERR_SCRATCH
+ * before anything is launched; so do all other argument errors of
+ * tl_linear_apply, with the same codes.
+ */
+size_t tl_noalloc_scratch_bytes(void);
+int tl_linear_apply_noalloc(const uint16_t *x, int64_t T, int64_t K, int64_t N, const int8_t *signs,
+                            const uint32_t *packed, const uint16_t *scales, const int8_t *q,
+                            const float *row_scale, void *y, int y_dtype, void *stream);
 
 #ifdef __cplusplus
 }

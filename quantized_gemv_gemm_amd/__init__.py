@@ -57,6 +57,9 @@ _SIGS = {
     "tl_linear_workspace_size": (_c_sz, [_c_i64, _c_i64, _c_i64]),
     "tl_linear_apply": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                        ctypes.c_int, _c_p, _c_sz, _c_p]),
+    "tl_noalloc_scratch_bytes": (_c_sz, []),
+    "tl_linear_apply_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                               _c_p, ctypes.c_int, _c_p]),
 }
 
 PATH_GEMV, PATH_INT8 = 0, 1
@@ -455,6 +458,38 @@ def linear_apply(x, packed, scales, q, row_scale, signs=None, out_dtype=None, ou
     _check("tl_linear_apply", lib().tl_linear_apply(
         _ptr(x), T, K, N, _ptr(signs), _ptr(packed), _ptr(scales), _ptr(q), _ptr(row_scale), _ptr(out), code,
         _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the static per-GPU scratch array behind linear_apply_noalloc."""
+    return int(lib().tl_noalloc_scratch_bytes())
+
+
+def linear_apply_noalloc(x, packed, scales, q, row_scale, signs=None, out_dtype=None, out=None):
+    """linear_apply without a workspace: the library's static per-GPU scratch array
+    serves instead (same kernels, same outputs).  Calls that overlap in time on
+    one GPU share that array and race.  ``out`` may be given so that the call
+    allocates nothing at all."""
+    import torch
+    _check_x(x, signs)
+    _need(scales, "scales", torch.float16, 2)
+    _need(q, "q", torch.int8, 2)
+    _need(row_scale, "row_scale", torch.float32, 1)
+    T, K = x.shape
+    N = scales.shape[0]
+    _check_packed(packed, N, K)
+    if scales.shape != (N, K // GROUP) or q.shape != (N, K // GROUP) or row_scale.shape != (N,):
+        raise ValueError("shape mismatch in linear_apply_noalloc")
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype or torch.bfloat16, device=x.device)
+    code = _out_code(out.dtype)
+    _need(out, "out", out.dtype, 2)
+    if out.shape != (T, N):
+        raise ValueError("out must be [T, N]")
+    _check("tl_linear_apply_noalloc", lib().tl_linear_apply_noalloc(
+        _ptr(x), T, K, N, _ptr(signs), _ptr(packed), _ptr(scales), _ptr(q), _ptr(row_scale), _ptr(out), code,
+        _stream(x.device)))
     return out
 
 

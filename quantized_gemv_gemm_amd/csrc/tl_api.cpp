@@ -63,6 +63,8 @@ const char *tl_status_string(int s) {
     case TL_ERR_UNSUPPORTED: return "no kernel variant for this request";
     case TL_ERR_WORKSPACE: return "workspace missing or too small";
     case TL_ERR_ALIAS: return "an output overlaps an input or another output";
+    case TL_ERR_SCRATCH:
+      return "request needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -323,6 +325,8 @@ int tl_gemm_int8_rescale(const int8_t *xq, const float *tok_scale, int64_t M, in
                                   acc_out, workspace, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
 // ---------------------------------------------------------------------------
 // whole layer from the raw input, path chosen by the token count
 // ---------------------------------------------------------------------------
@@ -355,6 +359,57 @@ LinearLayout linear_layout(int64_t T, int64_t K, int64_t N) {
 
 }  // namespace
 
+namespace tl {
+
+size_t linear_scratch_bytes(int64_t T, int64_t K, int64_t N) { return linear_layout(T, K, N).total; }
+
+int linear_check(const uint16_t *x, int64_t T, int64_t K, int64_t N, const uint32_t *packed,
+                 const uint16_t *scales, const int8_t *q, const float *row_scale, void *y, int y_dtype) {
+  if (T < 0 || N < 0 || K <= 0 || K % tl::kHBlock || T >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return TL_ERR_SHAPE;
+  if (!tl::fused_input_supported(K)) return TL_ERR_UNSUPPORTED;
+  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (T == 0 || N == 0) return TL_OK;
+  if (!x || !packed || !scales || !q || !row_scale || !y) return TL_ERR_NULLPTR;
+  return TL_OK;
+}
+
+int linear_run(const uint16_t *x, int64_t T, int64_t K, int64_t N, const int8_t *signs,
+               const uint32_t *packed, const uint16_t *scales, const int8_t *q, const float *row_scale,
+               void *y, int y_dtype, void *workspace, size_t workspace_bytes, hipStream_t st) {
+  const LinearLayout l = linear_layout(T, K, N);
+  if (!workspace || workspace_bytes < l.total) return TL_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(q) ||
+      !aligned16(row_scale) || !aligned16(y) || !aligned16(workspace) || (signs && !aligned16(signs)))
+    return TL_ERR_ALIGN;
+  const size_t G = size_t(K / tl::kGroup);
+  const size_t ysz = size_t(T) * N * (y_dtype == TL_F32 ? 4 : 2);
+  Span in[] = {{x, size_t(T) * K * 2}, {signs, signs ? size_t(K) : 0u},
+               {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2},
+               {q, size_t(N) * G}, {row_scale, size_t(N) * 4}};
+  Span out[] = {{y, ysz}, {workspace, l.total}};
+  if (any_alias(in, 6, out, 2)) return TL_ERR_ALIAS;
+  char *ws = static_cast<char *>(workspace);
+  if (l.path == TL_PATH_GEMV) {
+    if (tl::gemv_rot_supported(T, K, N))
+      return from_hip(tl::launch_gemv_rot(x, T, K, N, signs, packed, scales, y, y_dtype, st));
+    void *gw = ws + kLinCounters;
+    hipError_t e = tl::launch_gemv_prepare_rotated(x, T, K, signs, gw, st);
+    if (e != hipSuccess) return from_hip(e);
+    return from_hip(tl::launch_gemv_main(gw, T, K, N, packed, scales, y, y_dtype, st));
+  }
+  int8_t *xq = reinterpret_cast<int8_t *>(ws + l.xq);
+  float *sx = reinterpret_cast<float *>(ws + l.sx);
+  hipError_t e = tl::launch_quant_x(x, T, K, signs, xq, sx, st);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(tl::launch_gemm(xq, sx, T, K, N, packed, q, row_scale, y, y_dtype, nullptr,
+                                  l.gemm_ws ? workspace : nullptr, st));
+}
+
+}  // namespace tl
+
+extern "C" {
+
 int tl_linear_path(int64_t T, int64_t K, int64_t N) {
   if (T <= tl::kTokChunk) return TL_PATH_GEMV;
   if (T > tl::kGemvMaxTokens) return TL_PATH_INT8;
@@ -376,40 +431,10 @@ int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const in
                     const uint32_t *packed, const uint16_t *scales, const int8_t *q,
                     const float *row_scale, void *y, int y_dtype, void *workspace,
                     size_t workspace_bytes, void *stream) {
-  if (T < 0 || N < 0 || K <= 0 || K % tl::kHBlock || T >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
-    return TL_ERR_SHAPE;
-  if (!tl::fused_input_supported(K)) return TL_ERR_UNSUPPORTED;
-  if (y_dtype != TL_BF16 && y_dtype != TL_F32) return TL_ERR_DTYPE;
+  if (int s = tl::linear_check(x, T, K, N, packed, scales, q, row_scale, y, y_dtype)) return s;
   if (T == 0 || N == 0) return TL_OK;
-  if (!x || !packed || !scales || !q || !row_scale || !y) return TL_ERR_NULLPTR;
-  const LinearLayout l = linear_layout(T, K, N);
-  if (!workspace || workspace_bytes < l.total) return TL_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(packed) || !aligned16(scales) || !aligned16(q) ||
-      !aligned16(row_scale) || !aligned16(y) || !aligned16(workspace) || (signs && !aligned16(signs)))
-    return TL_ERR_ALIGN;
-  const size_t G = size_t(K / tl::kGroup);
-  const size_t ysz = size_t(T) * N * (y_dtype == TL_F32 ? 4 : 2);
-  Span in[] = {{x, size_t(T) * K * 2}, {signs, signs ? size_t(K) : 0u},
-               {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2},
-               {q, size_t(N) * G}, {row_scale, size_t(N) * 4}};
-  Span out[] = {{y, ysz}, {workspace, l.total}};
-  if (any_alias(in, 6, out, 2)) return TL_ERR_ALIAS;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char *ws = static_cast<char *>(workspace);
-  if (l.path == TL_PATH_GEMV) {
-    if (tl::gemv_rot_supported(T, K, N))
-      return from_hip(tl::launch_gemv_rot(x, T, K, N, signs, packed, scales, y, y_dtype, st));
-    void *gw = ws + kLinCounters;
-    hipError_t e = tl::launch_gemv_prepare_rotated(x, T, K, signs, gw, st);
-    if (e != hipSuccess) return from_hip(e);
-    return from_hip(tl::launch_gemv_main(gw, T, K, N, packed, scales, y, y_dtype, st));
-  }
-  int8_t *xq = reinterpret_cast<int8_t *>(ws + l.xq);
-  float *sx = reinterpret_cast<float *>(ws + l.sx);
-  hipError_t e = tl::launch_quant_x(x, T, K, signs, xq, sx, st);
-  if (e != hipSuccess) return from_hip(e);
-  return from_hip(tl::launch_gemm(xq, sx, T, K, N, packed, q, row_scale, y, y_dtype, nullptr,
-                                  l.gemm_ws ? workspace : nullptr, st));
+  return tl::linear_run(x, T, K, N, signs, packed, scales, q, row_scale, y, y_dtype, workspace,
+                        workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -89,4 +89,13 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
                        const uint32_t *packed, const int8_t *q, const float *row_scale, void *y,
                        int y_dtype, int32_t *acc_out, void *workspace, hipStream_t stream);
 
+// whole layer from the raw input (tl_api.cpp): the checks that need no workspace,
+// then the workspace checks and the launches on the path tl_linear_path names
+size_t linear_scratch_bytes(int64_t T, int64_t K, int64_t N);
+int linear_check(const uint16_t *x, int64_t T, int64_t K, int64_t N, const uint32_t *packed,
+                 const uint16_t *scales, const int8_t *q, const float *row_scale, void *y, int y_dtype);
+int linear_run(const uint16_t *x, int64_t T, int64_t K, int64_t N, const int8_t *signs,
+               const uint32_t *packed, const uint16_t *scales, const int8_t *q, const float *row_scale,
+               void *y, int y_dtype, void *workspace, size_t workspace_bytes, hipStream_t st);
+
 }  // namespace tl
