@@ -158,48 +158,42 @@ __device__ __forceinline__ void select_chunk(PL &limbs, PS &sigma, PY &y, int &b
   b = min(kTokChunk, b - kTokChunk * c);
 }
 
-// one group for RB row blocks: two 64-k halves x two limbs, then f32 accumulation.
-// w0/w1 are the lane's packed words for the group's two 64-k halves.
-template <int RB, int NT, bool LP>
-__device__ __forceinline__ void group_mfma(const v4i (&ah)[2], const v4i (&al)[2],
-                                           const uint32_t (&w0)[RB], const uint32_t (&w1)[RB],
-                                           const float (&s)[RB], float (&acc)[RB][4]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const v4i z = {0, 0, 0, 0};
-    const v4i b0 = unpack_x64(w0[rb]);
-    const v4i b1 = unpack_x64(w1[rb]);
-    if (LP) {
-      v4i d = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[0], b0, z, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[1], b1, d, 0, 0, 0);
-      acc[rb][0] = fmaf(s[rb], (float)(d[0] * 256 + d[1]), acc[rb][0]);
-      acc[rb][1] = fmaf(s[rb], (float)(d[2] * 256 + d[3]), acc[rb][1]);
-      continue;
-    }
-    v4i dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[0], b0, z, 0, 0, 0);
-    v4i dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[0], b0, z, 0, 0, 0);
-    dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[1], b1, dh, 0, 0, 0);
-    dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[1], b1, dl, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) acc[rb][i] = fmaf(s[rb], (float)(dh[i] * 256 + dl[i]), acc[rb][i]);
-  }
-}
-
-// both groups of a pair: tile words .x/.y feed group 2p, .z/.w group 2p+1
+// both groups of a pair: tile words .x/.y feed group 2p, .z/.w group 2p+1.  With
+// paired limbs each group is a single chain, so the two groups' chains are issued
+// interleaved (first halves, then second halves): one chain's matrix instruction
+// runs while the other's result is pending.
 template <int RB, int NT, bool LP>
 __device__ __forceinline__ void pair_mfma(const v4i (&ah)[2][2], const v4i (&al)[2][2],
                                           const uint4 (&w)[RB], const float (&s)[2][RB],
                                           float (&acc)[RB][4]) {
-  uint32_t a0[RB], a1[RB], b0[RB], b1[RB];
+  const v4i z = {0, 0, 0, 0};
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    a0[rb] = w[rb].x;
-    a1[rb] = w[rb].y;
-    b0[rb] = w[rb].z;
-    b1[rb] = w[rb].w;
+    const v4i a0 = unpack_x64(w[rb].x), a1 = unpack_x64(w[rb].y);  // group 2p
+    const v4i b0 = unpack_x64(w[rb].z), b1 = unpack_x64(w[rb].w);  // group 2p + 1
+    if (LP) {  // one chain per group: interleaved
+      v4i d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[0][0], a0, z, 0, 0, 0);
+      v4i d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[1][0], b0, z, 0, 0, 0);
+      d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[0][1], a1, d0, 0, 0, 0);
+      d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[1][1], b1, d1, 0, 0, 0);
+      acc[rb][0] = fmaf(s[0][rb], (float)(d0[0] * 256 + d0[1]), acc[rb][0]);
+      acc[rb][1] = fmaf(s[0][rb], (float)(d0[2] * 256 + d0[3]), acc[rb][1]);
+      acc[rb][0] = fmaf(s[1][rb], (float)(d1[0] * 256 + d1[1]), acc[rb][0]);
+      acc[rb][1] = fmaf(s[1][rb], (float)(d1[2] * 256 + d1[3]), acc[rb][1]);
+      continue;
+    }
+    // two limbs: each group already has two independent chains (hi, lo)
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const v4i c0 = gi ? b0 : a0, c1 = gi ? b1 : a1;
+      v4i dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[gi][0], c0, z, 0, 0, 0);
+      v4i dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[gi][0], c0, z, 0, 0, 0);
+      dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(ah[gi][1], c1, dh, 0, 0, 0);
+      dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[gi][1], c1, dl, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[rb][i] = fmaf(s[gi][rb], (float)(dh[i] * 256 + dl[i]), acc[rb][i]);
+    }
   }
-  group_mfma<RB, NT, LP>(ah[0], al[0], a0, a1, s[0], acc);
-  group_mfma<RB, NT, LP>(ah[1], al[1], b0, b1, s[1], acc);
 }
 
 // the lane's 16 bytes of tile (row block rbg, pair p): one coalesced kilobyte per wave
@@ -276,16 +270,59 @@ __device__ __forceinline__ void lds_wait(v4i (&ah)[2][2], v4i (&al)[2][2], uint3
   for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(sb[0][rb]), "+v"(sb[1][rb]));
 }
 
+// as lds_wait, leaving the last N LDS reads (those of the next pair) in flight
+template <int N, int RB>
+__device__ __forceinline__ void lds_wait_n(v4i (&ah)[2][2], v4i (&al)[2][2], uint32_t (&sb)[2][RB], bool lp) {
+  asm volatile("s_waitcnt lgkmcnt(%4)"
+               : "+v"(ah[0][0]), "+v"(ah[0][1]), "+v"(ah[1][0]), "+v"(ah[1][1])
+               : "n"(N));
+  if (!lp) asm volatile("" : "+v"(al[0][0]), "+v"(al[0][1]), "+v"(al[1][0]), "+v"(al[1][1]));
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) asm volatile("" : "+v"(sb[0][rb]), "+v"(sb[1][rb]));
+}
+
+// the LDS operands of one pair: A fragments (limbs staged in LDS) and the two
+// groups' scales of the RB row blocks
+template <int RB, bool LP, bool ALDS>
+__device__ __forceinline__ void pair_lds_issue(int p, int G, const int8_t *lah, const int8_t *lal, const char *ls,
+                                               int col, v4i (&ah)[2][2], v4i (&al)[2][2], uint32_t (&sb)[2][RB]) {
+  constexpr int kGS = LP ? 128 : 4096, kHS = LP ? 16 : 2048;  // group and half strides
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int gl = min(2 * p + gi, G - 1);
+    if (ALDS) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ah[gi][h] = lds_read16(lah + kGS * gl + kHS * h);
+        if (!LP) al[gi][h] = lds_read16(lal + kGS * gl + kHS * h);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sb[gi][rb] = lds_read_u16(ls + 2 * ((16 * rb + col) * G + gl));
+  }
+}
+
 __host__ __device__ constexpr int scale_lds_bytes(int rows, int G) {
   return (rows * G * 2 + 1023) / 1024 * 1024;
 }
 
-// partial sums of the W waves -> LDS -> wave 0 scales by sigma/64 and stores
+// sigma_t / 64 for the token of each accumulator of the lane (0 past b), read when
+// the kernel starts so that no load is left for the end of the workgroup
+template <int NT, bool LP>
+__device__ __forceinline__ void token_scales(const float *__restrict__ sigma, int b, int lane, float (&tsc)[4]) {
+  const int qd = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = LP ? 2 * qd + i : 4 * i + qd;
+    tsc[i] = i < NT && t < b ? sigma[t] * (1.0f / 64.0f) : 0.0f;
+  }
+}
+
+// partial sums of the W waves -> LDS -> wave 0 scales by sigma/64 (tsc) and stores
 template <int RB, int NT, bool LP>
 __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red, int W, int wave,
                                                  int lane, int b, int64_t n0, int64_t N,
-                                                 const float *__restrict__ sigma, void *y,
-                                                 int y_dtype) {
+                                                 const float (&tsc)[4], void *y, int y_dtype) {
   const int col = lane & 15, qd = lane >> 4;
   if (W > 1) {
     if (wave > 0) {
@@ -306,7 +343,7 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red
   for (int i = 0; i < NT; ++i) {
     const int t = LP ? 2 * qd + i : 4 * i + qd;  // token of accumulator i
     if (t >= b) continue;
-    const float sc = sigma[t] * (1.0f / 64.0f);
+    const float sc = tsc[i];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int64_t n = n0 + 16 * rb + col;
@@ -353,6 +390,8 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
   constexpr int NA = LP ? 4 : 8;  // A fragment loads per pair when not ALDS
   extern __shared__ __attribute__((aligned(16))) char smem[];
   select_chunk(limbs, sigma, y, b, K, N, y_dtype);
+  float tsc[4];
+  token_scales<NT, LP>(sigma, b, threadIdx.x & 63, tsc);
   const int64_t region = LP ? limb_region_bytes(b, K) : 32 * K;  // this chunk's limbs
   int8_t *lx = reinterpret_cast<int8_t *>(smem);
   char *ls = smem + (ALDS ? lds_limb_bytes : 0);
@@ -420,32 +459,37 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
   // 4. pairs in arrival order.  LDS is read through lds_read* so that the
   //    compiler, which cannot tell these reads from the destinations of the
   //    direct loads, does not make each of them wait for every register load.
+  //    The next pair's LDS reads are issued before this pair's matrix
+  //    instructions (two register slots), so their latency overlaps the work.
   float acc[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[rb][i] = 0.0f;
+  constexpr int kLdsPerPair = (ALDS ? (LP ? 4 : 8) : 0) + 2 * RB;
+  // the second slot costs registers: only where the estimate (tiles, both slots,
+  // accumulators, addressing) stays inside the variant's budget; and the wait
+  // count field holds up to 15
+  constexpr int kRegs = PMAX * RB * 4 + (ALDS ? 2 * (LP ? 16 : 32) : 0) + 8 * RB + 48;
+  constexpr bool kPipe =
+      kLdsPerPair <= 15 && (!ALDS || kRegs <= (stream_heavy(ALDS, RB, PMAX, LP) ? 256 : 128));
+  v4i ahs[2][2][2], als[2][2][2];             // [slot][group][64-k half]
+  uint32_t sbs[2][2][RB];
+  if (kPipe) pair_lds_issue<RB, LP, ALDS>(p_begin, G, lah, lal, ls, col, ahs[0], als[0], sbs[0]);
 #pragma unroll
   for (int pi = 0; pi < PMAX; ++pi) {
     const bool live = pi < np;
     const int p = p_begin + (live ? pi : np - 1);
-    v4i ah[2][2], al[2][2];
-    uint32_t sb[2][RB];
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int gl = min(2 * p + gi, G - 1);
-      if (ALDS) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          ah[gi][h] = lds_read16(lah + kGS * gl + kHS * h);
-          if (!LP) al[gi][h] = lds_read16(lal + kGS * gl + kHS * h);
-        }
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-        sb[gi][rb] = lds_read_u16(ls + 2 * ((16 * rb + col) * G + gl));
+    const int sl = kPipe ? (pi & 1) : 0;
+    if (kPipe && pi + 1 < PMAX) {
+      const int pn = p_begin + (pi + 1 < np ? pi + 1 : np - 1);
+      pair_lds_issue<RB, LP, ALDS>(pn, G, lah, lal, ls, col, ahs[sl ^ 1], als[sl ^ 1], sbs[sl ^ 1]);
+      lds_wait_n<kPipe ? kLdsPerPair : 0, RB>(ahs[sl], als[sl], sbs[sl], LP || !ALDS);
+    } else {
+      if (!kPipe) pair_lds_issue<RB, LP, ALDS>(p, G, lah, lal, ls, col, ahs[sl], als[sl], sbs[sl]);
+      lds_wait_n<0, RB>(ahs[sl], als[sl], sbs[sl], LP || !ALDS);
     }
-    lds_wait<RB>(ah, al, sb, LP || !ALDS);
+    v4i ah[2][2], al[2][2];
     if (!ALDS) {
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
@@ -454,22 +498,25 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
           ah[gi][h] = ga[ALDS ? 0 : pi][gi][h][0];
           al[gi][h] = ga[ALDS ? 0 : pi][gi][h][LP ? 0 : 1];
         }
-    } else if (LP) {
+    } else {
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) al[gi][h] = ah[gi][h];
+        for (int h = 0; h < 2; ++h) {
+          ah[gi][h] = ahs[sl][gi][h];
+          al[gi][h] = LP ? ahs[sl][gi][h] : als[sl][gi][h];
+        }
     }
     float sv[2][RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      sv[0][rb] = live ? half_bits_to_float(uint16_t(sb[0][rb])) : 0.0f;
-      sv[1][rb] = live && 2 * p + 1 < G ? half_bits_to_float(uint16_t(sb[1][rb])) : 0.0f;
+      sv[0][rb] = live ? half_bits_to_float(uint16_t(sbs[sl][0][rb])) : 0.0f;
+      sv[1][rb] = live && 2 * p + 1 < G ? half_bits_to_float(uint16_t(sbs[sl][1][rb])) : 0.0f;
     }
     pair_mfma<RB, NT, LP>(ah, al, wv[pi], sv, acc);
   }
   __syncthreads();  // every wave is done with LDS before `red` is written
-  reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, sigma, y, y_dtype);
+  reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
 }
 
 // --------------------------------------------------------------------------
@@ -608,7 +655,9 @@ __global__ __launch_bounds__(q8_heavy(ALDS, RB, PMAX) ? 512 : 1024) void gemv_q8
     group_mfma_q8<RB, NT>(a[1], w10, w11, s1, acc);
   }
   __syncthreads();  // every wave is done with LDS before `red` is written
-  reduce_and_store<RB, NT, false>(acc, red, W, wave, lane, b, n0, N, tok_scale, y, y_dtype);
+  float tsc[4];
+  token_scales<NT, false>(tok_scale, b, lane, tsc);
+  reduce_and_store<RB, NT, false>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
 }
 
 // --------------------------------------------------------------------------
@@ -659,6 +708,8 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
     void *__restrict__ y, int y_dtype) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   select_chunk(limbs, sigma, y, b, K, N, y_dtype);
+  float tsc[4];
+  token_scales<NT, LP>(sigma, b, threadIdx.x & 63, tsc);
   char *ls = smem;  // scale block of the workgroup's rows, then (W - 1) * RB * NT * 64 floats
   float *red = reinterpret_cast<float *>(smem + scale_lds_bytes(16 * RB, int(K / kGroup)));
   const int W = blockDim.x >> 6;
@@ -704,7 +755,7 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
       if (p + 3 < p_end) load_pair<RB, LP>(sl[1], p + 3, G, GP, ah, al, packed, rbg, lane);
     }
   }
-  reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, sigma, y, y_dtype);
+  reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
 }
 
 // --------------------------------------------------------------------------
