@@ -151,6 +151,40 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(out, indent=1))
 
 
+def spread(samples_ms, run_medians_ms):
+    """p10 / p50 / p90 (us) of the per-step samples of one arm, and the median of each run."""
+    a = np.asarray(samples_ms, dtype=np.float64) * 1e3
+    return {"us_p10": round(float(np.percentile(a, 10)), 3), "us_p50": round(float(np.percentile(a, 50)), 3),
+            "us_p90": round(float(np.percentile(a, 90)), 3),
+            "us_run_medians": [round(m * 1e3, 3) for m in run_medians_ms]}
+
+
+def roofline_gate(out):
+    """Any rate above the chip's peak means a measurement artefact (a launch that did
+    not do its work, or data served from a cache): such a line is not valid."""
+    bad = []
+    for b, v in out["decode_gemv_by_b"].items():
+        if v["GBps"] > HBM_PEAK_GBS:
+            bad.append(f"decode_gemv b={b} {v['GBps']} GB/s")
+    for b, v in out.get("decode_layer", {}).items():
+        if v["GBps"] > HBM_PEAK_GBS:
+            bad.append(f"decode_layer b={b} {v['GBps']} GB/s")
+    for k, v in out["prefill_gemm"].items():
+        if v["TOPs"] > INT8_PEAK_TOPS:
+            bad.append(f"prefill_gemm {k} {v['TOPs']} TOP/s")
+    rc = out["launch_floor"].get("read_codes")
+    if rc and rc["GBps"] > HBM_PEAK_GBS:
+        bad.append(f"read floor {rc['GBps']} GB/s")
+    st = out.get("stack64")
+    if st:
+        if st["decode_b16"]["gemv_GBps"] > HBM_PEAK_GBS:
+            bad.append("stack64 decode")
+        if st["prefill_m2048"]["gemm_TOPs"] > INT8_PEAK_TOPS:
+            bad.append("stack64 prefill")
+    return {"rule": f"every GB/s <= {HBM_PEAK_GBS:.0f} and every TOP/s <= {INT8_PEAK_TOPS:.0f}",
+            "valid": not bad, "violations": bad}
+
+
 def load_traffic():
     """Per-launch HBM traffic measured for the current kernel sources, or {} if absent or stale."""
     try:
@@ -303,17 +337,26 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
     # per-kernel device times: the same steps again, each timed group queued
-    # behind a spin (the step time above is the plain, spin-free pass)
-    rec = []
-    for _ in range(args.steps):
-        step(rec, spin=True)
-    torch.cuda.synchronize()
-
+    # behind a spin (the step time above is the plain, spin-free pass); two such
+    # runs, so that every arm has two medians from the same session
     gemv_ms = {b: [] for b in DECODE_BS}
     gemm_ms = {"gate_up": [], "down": []}
-    sink = {"gemv": gemv_ms, "gemm": gemm_ms}
-    for kind, key, n, e0, e1 in rec:
-        sink[kind][key].append(e0.elapsed_time(e1) / n)
+    gemv_runs = {b: [] for b in DECODE_BS}
+    gemm_runs = {"gate_up": [], "down": []}
+    for _run in range(2):
+        rec = []
+        for _ in range(args.steps):
+            step(rec, spin=True)
+        torch.cuda.synchronize()
+        sink = {"gemv": gemv_ms, "gemm": gemm_ms}
+        runs = {"gemv": gemv_runs, "gemm": gemm_runs}
+        this = {"gemv": {b: [] for b in DECODE_BS}, "gemm": {"gate_up": [], "down": []}}
+        for kind, key, n, e0, e1 in rec:
+            sink[kind][key].append(e0.elapsed_time(e1) / n)
+            this[kind][key].append(e0.elapsed_time(e1) / n)
+        for kind in ("gemv", "gemm"):
+            for key, v in this[kind].items():
+                runs[kind][key].append(float(np.median(v)))
 
     # the fused input kernels: n back-to-back launches between two events, all
     # queued behind a device-side spin so that the GPU never waits for the host
@@ -393,6 +436,33 @@ def main():
     floor["library_copy_codes"] = {"bytes_moved": int(nb), "us": round(t_copy * 1e6, 2),
                                    "GBps": round(nb / t_copy / 1e9, 1)}
     del codes_dst
+    # the streaming floor: one launch that only reads the qkv layer's packed codes
+    # (13.1 MB, rotating copies), shaped like the GEMV's weight stream
+    sink_t = torch.zeros((4,), dtype=torch.int32, device=dev)
+
+    def read_codes():
+        tl.read_probe(qkv[kq[0] % len(qkv)][0], sink_t)
+        kq[0] += 1
+    t_read = run_time(read_codes, n=DEC_LAYERS * 4) * 1e-3
+    nb = qkv[0][0].numel() * 4
+    floor["read_codes"] = {"bytes": int(nb), "us": round(t_read * 1e6, 2), "GBps": round(nb / t_read / 1e9, 1),
+                           "kernel": "read_probe"}
+    # the whole decode layer from the raw bf16 input (rotation, limbs, GEMV): one
+    # launch for b <= 2 at this shape, else the fused rotation + limb prep and the GEMV
+    layer = {}
+    for b in DECODE_BS:
+        kl = [0]
+
+        def one_layer():
+            packed, scales, _, _ = qkv[kl[0] % len(qkv)]
+            kl[0] += 1
+            tl.gemv_ternary_x(x_dec[b], packed, scales, out=y_dec[b], workspace=ws_dec[b])
+        t_l = run_time(one_layer, n=DEC_LAYERS * 4) * 1e-3
+        nbytes = gemv_bytes(b, Kq, Nq)   # bf16 input: 2 b K bytes, as many as the limbs
+        layer[str(b)] = {"us": round(t_l * 1e6, 2), "GBps": round(nbytes / t_l / 1e9, 1),
+                         "frac": round(nbytes / t_l / 1e9 / HBM_PEAK_GBS, 4),
+                         "path": tl.last_kernel_name() if tl.last_kernel_name().startswith("gemv_rot")
+                         else "gemv_prep_x + " + tl.last_kernel_name()}
     gc.enable()
 
     if os.environ.get("BENCH_DEBUG"):
@@ -405,7 +475,7 @@ def main():
         nbytes = gemv_bytes(b, Kq, Nq)
         by_b[str(b)] = {"us": round(t * 1e6, 3), "GBps": round(nbytes / t / 1e9, 1),
                         "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "kernel": kernel_names[("gemv", b)],
-                        "bytes": nbytes}
+                        "bytes": nbytes, **spread(gemv_ms[b], gemv_runs[b])}
         tot_bytes += nbytes
         tot_s += t
     dec_gbs = tot_bytes / tot_s / 1e9
@@ -416,7 +486,8 @@ def main():
         t = float(np.mean(gemm_ms[name])) * 1e-3
         ops = 2.0 * PREFILL_M * pre[name]["K"] * pre[name]["N"]
         pre_out[name] = {"us": round(t * 1e6, 2), "TOPs": round(ops / t / 1e12, 1),
-                         "frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4), "kernel": kernel_names[("gemm", name)]}
+                         "frac": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4), "kernel": kernel_names[("gemm", name)],
+                         **spread(gemm_ms[name], gemm_runs[name])}
         ops_tot += ops
         t_tot += t
     pre_tops = ops_tot / t_tot / 1e12
@@ -442,7 +513,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("cpu baseline: oracle decode qkv b=16")
+        log("cpu baseline: oracle decode qkv b=16, prefill gate_up and down M=512")
         cpu = cpu_baseline(args.cpu_seconds)
 
     out = {
@@ -488,6 +559,8 @@ def main():
         "stack64": stack,
         "cpu_baseline": cpu,
     }
+    out["decode_layer"] = layer
+    out["gate"] = roofline_gate(out)
     print(json.dumps(out), flush=True)
 
 
@@ -728,28 +801,84 @@ def stack_pass(tl, torch, dev, steps, log):
     return out
 
 
+def host_info():
+    """CPU model and the cores this process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": int(avail), "os_cpu_count": os.cpu_count()}
+
+
+def _timed(fn, seconds, max_reps=1000):
+    """Mean wall time of fn over repeats filling about `seconds` (at least one)."""
+    reps, t = 0, 0.0
+    while reps == 0 or (t < seconds and reps < max_reps):
+        s = time.perf_counter()
+        fn()
+        t += time.perf_counter() - s
+        reps += 1
+    return t / reps, reps
+
+
 def cpu_baseline(seconds):
-    """The oracle (numpy binary64) on the decode qkv layer at b=16, repeated for ~`seconds`."""
+    """The oracle (numpy binary64, as it stands) on the bench's workloads, on the host:
+    decode qkv at b = 16 (rotation + GEMV) and the 512-token prefill of gate_up and
+    down (rotation, per-token int8, int GEMM, rescale; the scale decomposition is
+    load-time work, not timed, as on the GPU), with every BLAS thread and with one.
+    The one-thread prefill runs on the first 64 tokens of the chunk (a bounded
+    sample; rates are per token and so comparable)."""
+    import threadpoolctl
+
     import oracle
     import synth
-    try:
-        import threadpoolctl
-        cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
-    except Exception:
-        cores = os.cpu_count()
+    blas = [i for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas"]
+    threads = max(i["num_threads"] for i in blas) if blas else (os.cpu_count() or 1)
     L = synth.LayerInputs(0, 1, 0, 5120, 10240)
     codes, scales = L.codes(), L.scales()
     x = synth.bf16_bits_to_f32(L.x(16))
-    reps, t = 0, 0.0
-    while t < seconds or reps == 0:
-        s = time.perf_counter()
+
+    def dec():
         oracle.gemv_ternary(oracle.rotate_exact(x), codes, scales)
-        t += time.perf_counter() - s
-        reps += 1
-    per = t / reps
-    return {"value": round(gemv_bytes(16, 5120, 10240) / per / 1e9, 3), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"decode qkv K=5120 N=10240 b=16 (rotation + GEMV), {reps} reps, {per * 1e3:.1f} ms each"}
+    dec_all, reps_all = _timed(dec, seconds * 0.3)
+    with threadpoolctl.threadpool_limits(1):
+        dec_one, reps_one = _timed(dec, seconds * 0.1)
+    del codes, scales
+    db = gemv_bytes(16, 5120, 10240)
+    prefill = {}
+    for name, li, K, N in (("gate_up", 0, 5120, 34816), ("down", 1, 17408, 5120)):
+        Lp = synth.LayerInputs(0, 3, li, K, N)
+        pc, ps = Lp.codes(), Lp.scales()
+        q, rs, _ = oracle.decompose_scales(ps)
+        xp = synth.bf16_bits_to_f32(synth.activations(0, 3, li, PREFILL_M, K))
+
+        def pre(xs):
+            xq, sx = oracle.quant_act_int8(oracle.rotate_f32(xs))
+            oracle.rescale(oracle.gemm_int8_acc(xq, pc, q), rs, sx)
+        t_all, _ = _timed(lambda: pre(xp), 0.0)
+        with threadpoolctl.threadpool_limits(1):
+            t_one, _ = _timed(lambda: pre(xp[:64]), 0.0)
+        prefill[name] = {"all_threads_s": round(t_all, 3),
+                         "all_threads_TOPs": round(2.0 * PREFILL_M * N * K / t_all / 1e12, 4),
+                         "one_thread_s_64_tokens": round(t_one, 3),
+                         "one_thread_TOPs": round(2.0 * 64 * N * K / t_one / 1e12, 4)}
+        del pc, ps, q, rs, xp
+    return {"value": round(db / dec_all / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"decode qkv K=5120 N=10240 b=16 (rotation + GEMV), {reps_all} reps, "
+                      f"{dec_all * 1e3:.1f} ms each, on {threads} BLAS threads; prefill M=512 gate_up and "
+                      f"down once each (one thread: 64 tokens)",
+            "one_thread": {"value": round(db / dec_one / 1e9, 3), "unit": "GB/s", "cores": 1, "reps": reps_one,
+                           "ms": round(dec_one * 1e3, 1)},
+            "prefill_m512": prefill, "host": host_info()}
 
 
 if __name__ == "__main__":

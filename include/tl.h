@@ -333,6 +333,17 @@ int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const in
                     size_t workspace_bytes, void *stream);
 
 /*
+ * tl_read_probe -- measurement helper, not a step of the layer: one launch that
+ * only reads `bytes` (a multiple of 16) from src, the way the decode GEMV streams
+ * its weights (1 KB per wavefront load, all of a wavefront's loads at once), and
+ * writes nothing but possibly one word of *sink.  Its duration is the floor a
+ * single launch reading that many bytes reaches on this chip (launch, first
+ * memory round trip and tail included), beside which the GEMV's launch time can
+ * be put.  src and sink are device pointers, 16-byte aligned.
+ */
+int tl_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
+/*
  * tl_linear_apply_noalloc -- tl_linear_apply without a workspace argument and
  * without any allocation, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid it.

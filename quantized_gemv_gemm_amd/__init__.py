@@ -58,6 +58,7 @@ _SIGS = {
     "tl_linear_apply": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                        ctypes.c_int, _c_p, _c_sz, _c_p]),
     "tl_noalloc_scratch_bytes": (_c_sz, []),
+    "tl_read_probe": (ctypes.c_int, [_c_p, _c_sz, _c_p, _c_p]),
     "tl_linear_apply_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                _c_p, ctypes.c_int, _c_p]),
 }
@@ -459,6 +460,15 @@ def linear_apply(x, packed, scales, q, row_scale, signs=None, out_dtype=None, ou
         _ptr(x), T, K, N, _ptr(signs), _ptr(packed), _ptr(scales), _ptr(q), _ptr(row_scale), _ptr(out), code,
         _ptr(workspace), workspace.numel(), _stream(x.device)))
     return out
+
+
+def read_probe(src, sink):
+    """Measurement helper: one launch that only reads the bytes of ``src`` (see
+    tl_read_probe); ``sink`` is a 4-byte (or larger) device tensor."""
+    if not (src.is_cuda and sink.is_cuda and src.is_contiguous()):
+        raise ValueError("read_probe needs contiguous device tensors")
+    nbytes = src.numel() * src.element_size() // 16 * 16
+    _check("tl_read_probe", lib().tl_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(src.device)))
 
 
 def noalloc_scratch_bytes() -> int:

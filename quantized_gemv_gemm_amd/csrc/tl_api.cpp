@@ -295,6 +295,16 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
   return from_hip(tl::launch_quant(xr, T, K, xq, tok_scale, static_cast<hipStream_t>(stream)));
 }
 
+int tl_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+  if (bytes < 16 || bytes % 16 || bytes / 16 / 512 > 0x7FFFFFFF) return TL_ERR_SHAPE;
+  if (!src || !sink) return TL_ERR_NULLPTR;
+  if (!aligned16(src) || !aligned16(sink)) return TL_ERR_ALIGN;
+  Span in[] = {{src, bytes}};
+  Span out[] = {{sink, 4}};
+  if (any_alias(in, 1, out, 1)) return TL_ERR_ALIAS;
+  return from_hip(tl::launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 size_t tl_gemm_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || N < 0 || K <= 0 || K % tl::kGroup) return 0;
   return tl::gemm_workspace_bytes(M, K, N);

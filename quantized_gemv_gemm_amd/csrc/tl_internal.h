@@ -84,6 +84,9 @@ hipError_t launch_hadamard_half(const uint16_t *x, int64_t T, int64_t ldx, const
 hipError_t launch_hadamard_join(const double *u_lo, const double *u_hi, int64_t T, int half, float *xr,
                                 int64_t ldxr, hipStream_t stream);
 
+// measurement helper: a launch that only reads `bytes` (k_probe.hip)
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,
                        const uint32_t *packed, const int8_t *q, const float *row_scale, void *y,
