@@ -768,6 +768,7 @@ struct GemvPlan {
   int lds_limb_bytes;
   size_t lds_bytes;
   const char *name;
+  bool ok;     // the variant fits the compute unit (LDS, workgroup size)
 };
 
 constexpr int kLdsLimbBudget = 96 * 1024;
@@ -805,15 +806,18 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   GemvPlan p{};
   const bool lp = b <= 8;
   // waves for PMAX pairs each, within the wave cap of the resulting variant
+  // waves for PMAX pairs each, within the wave cap of the resulting variant; false
+  // when even the largest pair count leaves more waves than the cap allows
   auto shape = [&](bool alds, int rb, int pmax) {
     for (;; ++pmax) {
       const int cap = stream_heavy(alds, rb, pmax, lp) ? 8 : kMaxWaves;
       const int waves = int((GP + pmax - 1) / pmax);
-      if (waves <= cap || pmax >= (alds ? kPmaxLds : kPmaxReg)) {
+      if (waves <= cap) {
         p.waves = waves;
         p.pmax = int((GP + waves - 1) / waves);
-        return;
+        return true;
       }
+      if (pmax >= (alds ? kPmaxLds : kPmaxReg)) return false;
     }
   };
   // Row blocks per workgroup, 1..4: the smallest whose workgroups are all resident
@@ -823,13 +827,16 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   // and gate_up launches at b = 1..16 (RB = 3 beat 4 by 7-14 % at b = 8 and 16).
   // Residency: the runtime's occupancy figure for the variant (its registers and
   // LDS), cached per variant.
+  // Row blocks that cannot be shaped, or whose LDS exceeds the compute unit's, are
+  // skipped; 0 when none is left.
   auto choose_rb = [&](bool alds, int pmax0, size_t lds_limbs) {
-    int best = 4;
+    int best = 0;
     int64_t best_cost = INT64_MAX;
     for (int rb = 1; rb <= 4; ++rb) {
-      shape(alds, rb, pmax0);
+      if (!shape(alds, rb, pmax0)) continue;
       const size_t lds = lds_limbs + scale_lds_bytes(16 * rb, int(G)) +
                          size_t(p.waves > 1 ? p.waves - 1 : 1) * rb * nt * 256;
+      if (lds > size_t(kLdsPerCU)) continue;
       int64_t per_cu = stream_resident(alds, rb, b, p.pmax, p.waves, lds);
       if (per_cu <= 0) {  // no answer from the runtime: bound by LDS and the register budget
         const int wave_cap = stream_heavy(alds, rb, p.pmax, lp) ? 8 : 16;
@@ -842,19 +849,21 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     }
     return best;
   };
-  if (limb_bytes <= kLdsLimbBudget && GP <= 8 * kPmaxLds) {
+  int rb = 0;
+  if (limb_bytes <= kLdsLimbBudget && GP <= 8 * kPmaxLds &&
+      (rb = choose_rb(true, b <= 4 ? 5 : 3, size_t(limb_bytes))) > 0) {
     // limbs in LDS.  Small batches: few waves with several pairs each, so that
     // pairs are computed while later ones arrive; b > 4: up to four row blocks
     // share one copy of the limbs.
     p.kind = 0;
     p.lds_limb_bytes = int(limb_bytes);
-    p.rb = choose_rb(true, b <= 4 ? 5 : 3, size_t(limb_bytes));
+    p.rb = rb;
     shape(true, p.rb, b <= 4 ? 5 : 3);
-  } else if (GP <= 8 * kPmaxReg) {
+  } else if (GP <= 8 * kPmaxReg && (rb = choose_rb(false, 2, 0)) > 0) {
     // limbs from L2 into registers, all pairs at once
     p.kind = 1;
     p.lds_limb_bytes = 0;
-    p.rb = choose_rb(false, 2, 0);
+    p.rb = rb;
     shape(false, p.rb, 2);
   } else {
     p.kind = 2;
@@ -872,6 +881,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
       {"gemv_ring_rb1", "gemv_ring_rb2", "gemv_ring_rb2", "gemv_ring_rb2"}};
   p.name = names[p.kind][p.rb - 1];
   p.chunks = int(chunks);
+  p.ok = p.lds_bytes <= size_t(kLdsPerCU) && p.waves >= 1 && 64 * p.waves <= 1024;
   return p;
 }
 
@@ -1210,6 +1220,10 @@ void launch_rot_t(int nblk, const uint16_t *x, const int8_t *signs, int64_t K, i
 
 }  // namespace
 
+bool gemv_supported(int64_t b, int64_t K, int64_t N) {
+  return b <= 0 || N <= 0 || plan_gemv(b, K, N).ok;
+}
+
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
   // two int8 limb planes [b, K + 16] and the per-token scales
   return align256(size_t(limb_region_bytes(b, K))) + align256(size_t(kGemvMaxTokens) * sizeof(float));
@@ -1264,6 +1278,7 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
                             hipStream_t stream) {
   const GemvWs w = carve(const_cast<void *>(workspace), b, K);
   const GemvPlan p = plan_gemv(b, K, N);
+  if (!p.ok) return hipErrorInvalidValue;
   const dim3 grid(unsigned((N + 16 * p.rb - 1) / (16 * p.rb)), unsigned(p.chunks));
   const GemvArgs a{&w, b, K, N, packed, scales, y, y_dtype, stream};
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls

@@ -178,6 +178,7 @@ int tl_gemv_prepared(const void *workspace, size_t workspace_bytes, int64_t b, i
   Span in[] = {{workspace, need}, {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2}};
   Span out[] = {{y, ysz}};
   if (any_alias(in, 3, out, 1)) return TL_ERR_ALIAS;
+  if (!tl::gemv_supported(b, K, N)) return TL_ERR_UNSUPPORTED;
   return from_hip(tl::launch_gemv_main(workspace, b, K, N, packed, scales, y, y_dtype,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -199,6 +200,7 @@ int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint
   Span in[] = {{xr, size_t(b) * K * 4}, {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2}};
   Span out[] = {{y, ysz}, {workspace, need}};
   if (any_alias(in, 3, out, 2)) return TL_ERR_ALIAS;
+  if (!tl::gemv_supported(b, K, N)) return TL_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = tl::launch_gemv_prepare(xr, b, K, workspace, st);
   if (e != hipSuccess) return from_hip(e);
@@ -242,6 +244,7 @@ int tl_gemv_ternary_x(const uint16_t *x, int64_t b, int64_t K, int64_t N, const 
                {packed, size_t(tl::packed_words(N, K)) * 4}, {scales, size_t(N) * G * 2}};
   Span out[] = {{y, ysz}, {workspace, need}};
   if (any_alias(in, 4, out, 2)) return TL_ERR_ALIAS;
+  if (!tl::gemv_rot_supported(b, K, N) && !tl::gemv_supported(b, K, N)) return TL_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (tl::gemv_rot_supported(b, K, N))
     return from_hip(tl::launch_gemv_rot(x, b, K, N, signs, packed, scales, y, y_dtype, st));
@@ -400,6 +403,8 @@ int linear_run(const uint16_t *x, int64_t T, int64_t K, int64_t N, const int8_t 
   Span out[] = {{y, ysz}, {workspace, l.total}};
   if (any_alias(in, 6, out, 2)) return TL_ERR_ALIAS;
   char *ws = static_cast<char *>(workspace);
+  if (l.path == TL_PATH_GEMV && !tl::gemv_rot_supported(T, K, N) && !tl::gemv_supported(T, K, N))
+    return TL_ERR_UNSUPPORTED;
   if (l.path == TL_PATH_GEMV) {
     if (tl::gemv_rot_supported(T, K, N))
       return from_hip(tl::launch_gemv_rot(x, T, K, N, signs, packed, scales, y, y_dtype, st));

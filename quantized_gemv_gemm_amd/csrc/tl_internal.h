@@ -50,6 +50,9 @@ __host__ __device__ inline int64_t limb_frag_offset(int t, int64_t k, int limb, 
 }
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t N);
+// false when the weight-stream variant for (b, K, N) would not fit a compute unit
+// (its LDS or workgroup size); the entry points then return TL_ERR_UNSUPPORTED
+bool gemv_supported(int64_t b, int64_t K, int64_t N);
 hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *workspace,
                                hipStream_t stream);
 hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t N,

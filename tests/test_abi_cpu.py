@@ -220,3 +220,24 @@ def test_split_block_rejections():
     assert L.tl_hadamard_join(FAKE, FAKE2, 2, 1, FAKE3, 514, None) == 3
     assert L.tl_hadamard_join(FAKE, FAKE2, 2, 1, FAKE2, 512, None) == 8
     assert L.tl_hadamard_join(FAKE, FAKE2, 0, 1, FAKE3, 512, None) == 0
+
+
+def test_gemv_plan_that_does_not_fit_is_unsupported():
+    """A weight-stream variant whose LDS would exceed a compute unit's 160 KB is
+    refused on the host (TL_ERR_UNSUPPORTED), before any launch: K = 409600 puts
+    3200 group scales of 32 rows (204 KB) into the long-K variant's LDS."""
+    L = tl.lib()
+    K, N = 409600, 8192
+    ws = L.tl_gemv_workspace_size(1, K, N)
+    assert ws > 0
+    big = ctypes.c_size_t(1 << 40)
+    assert L.tl_gemv_prepared(FAKE, big, 1, K, N, FAKE2, FAKE3, FAKE4, 1, None) == 6
+
+
+def test_read_probe_rejections():
+    L = tl.lib()
+    assert L.tl_read_probe(FAKE, 100, FAKE2, None) == 2      # not a multiple of 16
+    assert L.tl_read_probe(FAKE, 0, FAKE2, None) == 2
+    assert L.tl_read_probe(None, 1024, FAKE2, None) == 1
+    assert L.tl_read_probe(ODD, 1024, FAKE2, None) == 3
+    assert L.tl_read_probe(FAKE, 1024, FAKE, None) == 8      # sink inside the source
