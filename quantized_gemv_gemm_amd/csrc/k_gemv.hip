@@ -39,7 +39,9 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <string>
 #include <tuple>
+#include <vector>
 
 #include "rotate_dev.h"
 #include "tl_device.h"
@@ -796,6 +798,26 @@ int fit_rb(int64_t N, int64_t chunks, size_t lds_fixed, size_t lds_per_rb, int w
 // the launch helpers); 0 when the runtime cannot tell
 int stream_resident(bool alds, int rb, int64_t b, int pmax, int waves, size_t lds);
 
+// "gemv_stream_lds_rb1_w4p5": kind, row blocks per workgroup, waves and pairs per
+// wave (the ring keeps two pairs per wave in flight: "gemv_ring_rb2_w8").  Static
+// strings, built once.
+const char *variant_name(int kind, int rb, int waves, int pmax) {
+  static const std::vector<std::string> table = [] {
+    std::vector<std::string> t;
+    static const char *kinds[3] = {"gemv_stream_lds", "gemv_stream_reg", "gemv_ring"};
+    for (int k = 0; k < 3; ++k)
+      for (int r = 1; r <= 4; ++r)
+        for (int w = 0; w <= 16; ++w)
+          for (int m = 0; m <= kPmaxLds; ++m)
+            t.push_back(std::string(kinds[k]) + "_rb" + std::to_string(r) + "_w" + std::to_string(w) +
+                        (k == 2 ? "" : "p" + std::to_string(m)));
+    return t;
+  }();
+  if (kind < 0 || kind > 2 || rb < 1 || rb > 4 || waves < 0 || waves > 16 || pmax < 0 || pmax > kPmaxLds)
+    return "gemv_unnamed";
+  return table[((size_t(kind) * 4 + (rb - 1)) * 17 + waves) * (kPmaxLds + 1) + pmax].c_str();
+}
+
 GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   // more than 16 tokens: one grid row per chunk of 16, each shaped like b = 16
   const int64_t chunks = b > kTokChunk ? limb_chunks(b) : 1;
@@ -875,11 +897,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   }
   p.lds_bytes = size_t(p.lds_limb_bytes) + scale_lds_bytes(16 * p.rb, int(G)) +
                 size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * nt * 64 * sizeof(float);
-  static const char *names[3][4] = {
-      {"gemv_stream_lds_rb1", "gemv_stream_lds_rb2", "gemv_stream_lds_rb3", "gemv_stream_lds_rb4"},
-      {"gemv_stream_reg_rb1", "gemv_stream_reg_rb2", "gemv_stream_reg_rb3", "gemv_stream_reg_rb4"},
-      {"gemv_ring_rb1", "gemv_ring_rb2", "gemv_ring_rb2", "gemv_ring_rb2"}};
-  p.name = names[p.kind][p.rb - 1];
+  p.name = variant_name(p.kind, p.rb, p.waves, p.pmax);
   p.chunks = int(chunks);
   p.ok = p.lds_bytes <= size_t(kLdsPerCU) && p.waves >= 1 && 64 * p.waves <= 1024;
   return p;
