@@ -74,6 +74,9 @@ def parse():
                         "shapes, with int8 weights already expanded, beside this library's GEMM")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
+    p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                   help="print the per-launch median of every counter in rocprofv3 --pmc CSVs of this bench "
+                        "(--steps S --warmup W), one row per decode b and prefill shape, then exit")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="write the HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                         "counter CSVs of this bench (--steps S --warmup W) and of --calib-copy, then exit")
@@ -105,14 +108,53 @@ def _short_name(name):
     return m.group(1) if m else name[:80]
 
 
+def _attribute(rows):
+    """(launch, kernel, value) for the GEMV and GEMM launches of the bench steps, in order.
+
+    Launches are attributed by their order inside a step: DEC_LAYERS GEMV launches
+    for each b in DECODE_BS, then PRE_LAYERS GEMM launches for gate_up and for down.
+    The GEMV launches of the launch-cost fit follow the steps and are dropped."""
+    gemv = [(n, v) for n, v in rows if "gemv_stream_kernel" in n or "gemv_ring_kernel" in n]
+    gemm = [(n, v) for n, v in rows if "gemm_i8_kernel" in n]
+    gemv = gemv[:len(gemm) // (2 * PRE_LAYERS) * DEC_LAYERS * len(DECODE_BS)]
+    if not gemv or len(gemv) % (DEC_LAYERS * len(DECODE_BS)) or not gemm or len(gemm) % (2 * PRE_LAYERS):
+        raise SystemExit(f"unexpected launch counts: {len(gemv)} GEMV, {len(gemm)} GEMM")
+    out = []
+    for i, (name, v) in enumerate(gemv):
+        out.append(("gemv", str(DECODE_BS[(i // DEC_LAYERS) % len(DECODE_BS)]), _short_name(name), v))
+    for i, (name, v) in enumerate(gemm):
+        out.append(("gemm", ("gate_up", "down")[(i // PRE_LAYERS) % 2], _short_name(name), v))
+    return out
+
+
+def summarize_counters(paths):
+    """Median per launch of each counter, as a markdown table (counters summed over the chip)."""
+    import csv
+    table, counters = {}, []
+    for path in paths:
+        with open(path, newline="") as f:
+            rows = list(csv.DictReader(f))
+        for cname in sorted({r["Counter_Name"] for r in rows}):
+            sel = sorted((r for r in rows if r["Counter_Name"] == cname), key=lambda r: int(r["Dispatch_Id"]))
+            counters.append(cname)
+            for fam, key, kname, v in _attribute([(r["Kernel_Name"], float(r["Counter_Value"])) for r in sel]):
+                e = table.setdefault((fam, key), {"kernel": kname})
+                e.setdefault(cname, []).append(v)
+    print("| launch | kernel | launches | " + " | ".join(counters) + " |")
+    print("|---|---|---|" + "---|" * len(counters))
+    for (fam, key), e in table.items():
+        label = f"decode GEMV qkv b={key}" if fam == "gemv" else f"prefill GEMM {key}"
+        vals = " | ".join(f"{float(np.median(e[c])):.4g}" if c in e else "-" for c in counters)
+        print(f"| {label} | `{e['kernel']}` | {len(e[counters[0]])} | {vals} |")
+
+
 def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """HBM bytes per launch of the GEMV and GEMM kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE runs.
 
     The counters read KiB per dispatch.  Each is scaled by the factor that makes
     it read exactly CALIB_BYTES for the calibration kernel (an elementwise
     negation of CALIB_BYTES of float32: CALIB_BYTES read, CALIB_BYTES written).
-    Launches are attributed by their order inside a step: 8 GEMV launches for
-    each b in DECODE_BS, then PRE_LAYERS GEMM launches for gate_up and for down.
+    Launches are attributed as _attribute says.
     """
     def calib(path):
         vals = [v for name, v in _pmc_rows(path) if "neg" in name]
@@ -124,20 +166,8 @@ def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     out = {"copy_factor": {"fetch": round(f_fac, 4), "write": round(w_fac, 4)},
            "sources": {k: source_hash(k) for k in KERNEL_SOURCES}, "gemv": {}, "gemm": {}}
     for counter, path, fac in (("fetch", fetch_csv, f_fac), ("write", write_csv, w_fac)):
-        rows = _pmc_rows(path)
-        gemv = [(n, v) for n, v in rows if "gemv_stream_kernel" in n or "gemv_ring_kernel" in n]
-        gemm = [(n, v) for n, v in rows if "gemm_i8_kernel" in n]
-        # the steps come first; the GEMV launches of the launch-cost fit follow them
-        gemv = gemv[:len(gemm) // (2 * PRE_LAYERS) * DEC_LAYERS * len(DECODE_BS)]
-        if not gemv or len(gemv) % (DEC_LAYERS * len(DECODE_BS)) or not gemm or len(gemm) % (2 * PRE_LAYERS):
-            raise SystemExit(f"unexpected launch counts in {path}: {len(gemv)} GEMV, {len(gemm)} GEMM")
-        for i, (name, v) in enumerate(gemv):
-            b = str(DECODE_BS[(i // DEC_LAYERS) % len(DECODE_BS)])
-            e = out["gemv"].setdefault(b, {"kernel": _short_name(name), "fetch": [], "write": []})
-            e[counter].append(v * 1024.0 * fac)
-        for i, (name, v) in enumerate(gemm):
-            key = ("gate_up", "down")[(i // PRE_LAYERS) % 2]
-            e = out["gemm"].setdefault(key, {"kernel": _short_name(name), "fetch": [], "write": []})
+        for fam, key, kname, v in _attribute(_pmc_rows(path)):
+            e = out[fam].setdefault(key, {"kernel": kname, "fetch": [], "write": []})
             e[counter].append(v * 1024.0 * fac)
     for fam in ("gemv", "gemm"):
         for e in out[fam].values():
@@ -197,6 +227,9 @@ def load_traffic():
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
