@@ -1,9 +1,12 @@
-"""Build libtl.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree."""
+"""Build libtl.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and record each
+kernel's register, scratch and LDS use as the compiler reports it (_build/kernel_resources.json)."""
 from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import json
 import os
+import re
 import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,16 +30,38 @@ DEVICE = [
 ]
 
 
-def _compile(src: str) -> str:
+RESOURCES = os.path.join(BUILD, "kernel_resources.json")
+_FIELDS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+           "Occupancy [waves/SIMD]": "occupancy", "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+           "LDS Size [bytes/block]": "lds"}
+
+
+def _resources(remarks: str) -> dict:
+    """Per-kernel register, scratch and LDS figures from the compiler's
+    kernel-resource-usage remarks (mangled kernel name -> figures)."""
+    out, cur = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: +(.+?): (\S+) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None and key in _FIELDS:
+            cur[_FIELDS[key]] = int(val) if val.lstrip("-").isdigit() else val
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", src, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = False) -> str:
@@ -44,13 +69,20 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    resources = {}
+    for src, (_, res) in zip(srcs, done):
+        for name, fig in res.items():
+            resources[name] = dict(fig, source=os.path.basename(src))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(RESOURCES, "w") as f:
+        json.dump(resources, f, indent=1, sort_keys=True)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
     return LIB
