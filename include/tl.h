@@ -170,9 +170,15 @@ int tl_hadamard_join(const double *u_lo, const double *u_hi, int64_t T, int half
  *             16-byte aligned; its contents on entry do not matter.
  * Numerics: each weight is read once for all b tokens; group sums run on int8
  * matrix cores with each token's activations held as a 15-bit fixed-point value
- * split into two int8 limbs (scale amax_t / 32639), and group results are
- * accumulated in f32.  Relative Frobenius error against exact arithmetic is
- * about 3e-5 on the generator's data (bound used by the tests: 1e-3).
+ * split into two int8 limbs, scaled per token and 1024-wide block of K (scale
+ * |x|max / 32639 of that block), and group results are accumulated in f32.
+ * Relative Frobenius error against exact arithmetic is about 3e-5 on the
+ * generator's data (bound used by the tests: 1e-3).  In general each activation
+ * is off by at most 2^-16 of the largest magnitude in its own block (15 bits per
+ * block, whatever the other blocks hold), so the error of y[t, n] is at most
+ * about 2^-16 sum_g |s[n,g]| sum_{k in g} |code[n,k]| max_blk(k) |xr[t,.]|: the
+ * relative error stays near 3e-5 unless y itself is small against that sum
+ * (heavy cancellation) or a block's values spread over more than 15 bits.
  * One matrix-core operand holds 16 tokens: b > 16 runs ceil(b/16) chunks of 16
  * tokens side by side in the same launch, each streaming the weights itself
  * (chunks of one row range share an L2), so the time grows with the chunk count
@@ -188,8 +194,9 @@ int tl_gemv_ternary(const float *xr, int64_t b, int64_t K, int64_t N, const uint
  * The two stages of tl_gemv_ternary, for callers that apply several weight
  * matrices to the same rotated input (e.g. q/k/v or gate/up as separate
  * layers) or that time the stages apart:
- *   tl_gemv_prepare  writes the activation limbs and token scales of xr [b, K]
- *                    into the workspace (one kernel);
+ *   tl_gemv_prepare  writes the activation limbs and their per-block scales of
+ *                    xr [b, K] into the workspace (one kernel, one wavefront per
+ *                    token and 1024-block);
  *   tl_gemv_prepared runs the weight-streaming kernel on a workspace that
  *                    tl_gemv_prepare filled for the same b and K (one kernel).
  * tl_gemv_ternary(...) is exactly tl_gemv_prepare followed by tl_gemv_prepared.
@@ -248,10 +255,10 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
  *   except tl_gemv_ternary_x (and the GEMV path of tl_linear_apply) for one
  *   token with N <= 12288 or two tokens with N <= 6144, and K <= 6144: there a
  *   single kernel rotates, splits into limbs and runs the GEMV, each workgroup
- *   rotating the blocks it needs, with the limbs scaled per 1024-block instead
- *   of per token; its error against the exact layer is the same (about 3e-5)
- *   but its output is not bit-identical to the sequence, and the workspace
- *   (still required) is not used.
+ *   rotating the blocks it needs; its limbs are the same, but it adds the
+ *   group results in another order, so its output is not bit-identical to the
+ *   sequence (the same error against the exact layer, about 3e-5), and the
+ *   workspace (still required) is not used.
  * in  x       bf16 [b or T, K] raw layer input; signs as in tl_hadamard_blk.
  * Requires K % 1024 == 0 and K <= 65536 (TL_ERR_UNSUPPORTED above: use the
  * unfused calls); other arguments as in the unfused entry points.

@@ -51,13 +51,17 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr float kLimbRange = 32639.0f;  // 127 * 257: hi, lo of 256*hi + lo stay in int8
-constexpr int kRowPad = kLimbRowPad;    // bytes after each limb row: spreads LDS banks
+constexpr int kRowPad = kLimbRowPad;
+constexpr int kSigLds = 1024;  // stream kernels' LDS for a chunk's limb scales (16 tokens x 16 blocks)
+// LDS of the ring kernel for one chunk's limb scales: 16 tokens x the blocks of K
+__host__ __device__ constexpr int ring_sig_bytes(int64_t K) {
+  return int((16 * ((K + 1023) / 1024) * 4 + 255) / 256 * 256);
+}    // bytes after each limb row: spreads LDS banks
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // workspace: the limb region (limb_region_bytes: rows for b <= 8, operand order
-// for b > 8), then sigma[b]
+// for b > 8), then sigma[b][limb_blocks(K)]
 struct GemvWs {
   int8_t *xhi;
   float *sigma;
@@ -71,55 +75,29 @@ GemvWs carve(void *workspace, int64_t b, int64_t K) {
 }
 
 // --------------------------------------------------------------------------
-// prep: xr f32 [b, K] -> limb rows hi, lo and sigma[t] = amax_t / 32639
+// prep: xr f32 [b, K] -> limbs and sigma[t][j] = |x|max / 32639 of each 1024-block,
+// one wavefront per (token, block): no step waits for another block
 // --------------------------------------------------------------------------
-constexpr int kPrepThreads = 256;
-
-__global__ __launch_bounds__(kPrepThreads) void gemv_prep_kernel(const float *__restrict__ xr,
-                                                                 int64_t K, int64_t Kp, int b,
-                                                                 int8_t *__restrict__ xhi,
-                                                                 float *__restrict__ sigma) {
-  __shared__ float red[kPrepThreads / 64];
-  const int64_t t = blockIdx.x;
-  const float *row = xr + t * K;
-  float m = 0.0f;
-  for (int64_t i = 4 * threadIdx.x; i < K; i += 4 * kPrepThreads) {
-    const float4 v = *reinterpret_cast<const float4 *>(row + i);
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-  }
-  const float amax = block_max<kPrepThreads>(m, red);
-  const float inv = amax > 0.0f ? kLimbRange / amax : 0.0f;
-  if (threadIdx.x == 0) sigma[t] = amax / kLimbRange;
-  int8_t *hrow = xhi + t * Kp;
-  int8_t *lrow = xhi + (int64_t(b) + t) * Kp;
-  for (int64_t i = 16 * threadIdx.x; i < K; i += 16 * kPrepThreads) {
-    const float4 *src = reinterpret_cast<const float4 *>(row + i);
-    uint32_t hw[4], lw[4];
+__global__ __launch_bounds__(64) void gemv_prep_kernel(const float *__restrict__ xr, int64_t K, int64_t Kp,
+                                                       int b, int8_t *__restrict__ xhi,
+                                                       float *__restrict__ sigma) {
+  const int nbk = limb_blocks(K);
+  const int t = int(blockIdx.x / unsigned(nbk)), blk = int(blockIdx.x - unsigned(t * nbk));
+  const int lane = threadIdx.x;
+  const int64_t k0 = int64_t(blk) * kHBlock;
+  const int len = int(K - k0 < kHBlock ? K - k0 : kHBlock);
+  const float *row = xr + int64_t(t) * K + k0;
+  float v[16];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 v = src[c];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-      uint32_t h = 0, l = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        int q = (int)rintf(f[e] * inv);
-        q = q > 32639 ? 32639 : (q < -32639 ? -32639 : q);
-        const int hi = (q + 128) >> 8;  // floor division: lo lands in [-128, 127]
-        const int lo = q - hi * 256;
-        h |= (uint32_t)(hi & 0xFF) << (8 * e);
-        l |= (uint32_t)(lo & 0xFF) << (8 * e);
-      }
-      hw[c] = h;
-      lw[c] = l;
-    }
-    if (b > 8) {  // operand order: 16 consecutive k of one token are one lane's 16 bytes
-      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 0, K)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4 *>(xhi + limb_frag_offset(int(t), i, 1, K)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    } else {
-      *reinterpret_cast<uint4 *>(hrow + i) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4 *>(lrow + i) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-    }
+  for (int s = 0; s < 4; ++s) {
+    const int e = 256 * s + 4 * lane;
+    const float4 f = e < len ? *reinterpret_cast<const float4 *>(row + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[4 * s] = f.x;
+    v[4 * s + 1] = f.y;
+    v[4 * s + 2] = f.z;
+    v[4 * s + 3] = f.w;
   }
+  store_block_limbs(v, lane, t, b, K, Kp, k0, len, xhi, sigma + int64_t(t) * nbk + blk);
 }
 
 // --------------------------------------------------------------------------
@@ -155,7 +133,7 @@ __device__ __forceinline__ void select_chunk(PL &limbs, PS &sigma, PY &y, int &b
   const int c = blockIdx.y;
   if (c == 0) return;
   limbs += 32 * K * c;
-  sigma += kTokChunk * c;
+  sigma += int64_t(kTokChunk) * c * limb_blocks(K);
   y = static_cast<char *>(y) + int64_t(kTokChunk) * c * N * (y_dtype == TL_F32 ? 4 : 2);
   b = min(kTokChunk, b - kTokChunk * c);
 }
@@ -308,24 +286,51 @@ __host__ __device__ constexpr int scale_lds_bytes(int rows, int G) {
   return (rows * G * 2 + 1023) / 1024 * 1024;
 }
 
-// sigma_t / 64 for the token of each accumulator of the lane (0 past b), read when
-// the kernel starts so that no load is left for the end of the workgroup
+// base[t * stride] for the token t of each accumulator of the lane (token b - 1
+// past b: those accumulators are never stored).  base and stride are the same for
+// the whole wave, so the addresses are a scalar base plus a 32-bit lane offset.
+// The values are used as loaded, with nothing computed from them here, so that
+// no instruction right after the loads has to wait for them.
 template <int NT, bool LP>
-__device__ __forceinline__ void token_scales(const float *__restrict__ sigma, int b, int lane, float (&tsc)[4]) {
+__device__ __forceinline__ void token_scales(const float *__restrict__ base, int stride, int b, int lane,
+                                             float (&u)[4]) {
   const int qd = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = LP ? 2 * qd + i : 4 * i + qd;
-    tsc[i] = i < NT && t < b ? sigma[t] * (1.0f / 64.0f) : 0.0f;
+    u[i] = i < NT ? base[(t < b ? t : b - 1) * stride] : 0.0f;
   }
 }
 
-// partial sums of the W waves -> LDS -> wave 0 scales by sigma/64 (tsc) and stores
+// The sums of accumulator i, so far in units of limb scale ua, move to units ub
+// (the limb scale of the block that starts): acc *= ua / ub, with the hardware
+// reciprocal (within an ulp or so: far inside the layer's error).  A block of
+// zeros (ub = 0) adds nothing and keeps the units; ua = 0 means nothing has been
+// added yet.  ua becomes the new units.
+template <int RB>
+__device__ __forceinline__ void change_unit(float (&acc)[RB][4], int i, float &ua, float ub) {
+  const float r = ub > 0.0f ? ua * __builtin_amdgcn_rcpf(ub) : 1.0f;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb][i] *= r;
+  ua = ub > 0.0f ? ub : ua;
+}
+template <int RB, int NT>
+__device__ __forceinline__ void change_units(float (&acc)[RB][4], float (&ua)[4], const float (&ub)[4]) {
+#pragma unroll
+  for (int i = 0; i < NT; ++i) change_unit<RB>(acc, i, ua[i], ub[i]);
+}
+
+// each wave's partial sums times its own token scales tsc (the limb or token
+// scale and the 1/64 of the unpacked codes) -> LDS -> wave 0 adds them and stores
 template <int RB, int NT, bool LP>
 __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red, int W, int wave,
                                                  int lane, int b, int64_t n0, int64_t N,
                                                  const float (&tsc)[4], void *y, int y_dtype) {
   const int col = lane & 15, qd = lane >> 4;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[rb][i] *= tsc[i];
   if (W > 1) {
     if (wave > 0) {
 #pragma unroll
@@ -345,12 +350,11 @@ __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red
   for (int i = 0; i < NT; ++i) {
     const int t = LP ? 2 * qd + i : 4 * i + qd;  // token of accumulator i
     if (t >= b) continue;
-    const float sc = tsc[i];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int64_t n = n0 + 16 * rb + col;
       if (n >= N) continue;
-      const float v = acc[rb][i] * sc;
+      const float v = acc[rb][i];
       if (y_dtype == TL_F32)
         reinterpret_cast<float *>(y)[int64_t(t) * N + n] = v;
       else
@@ -388,26 +392,37 @@ template <int RB, int NT, int PMAX, bool LP, bool ALDS>
 __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_stream_kernel(
     const int8_t *__restrict__ limbs, const float *__restrict__ sigma, int b, int64_t K,
     int64_t Kp, int64_t N, const uint32_t *__restrict__ packed, const uint16_t *__restrict__ scales,
-    void *__restrict__ y, int y_dtype, int lds_limb_bytes) {
+    void *__restrict__ y, int y_dtype, int lds_limb_bytes, uint32_t wmagic) {
   constexpr int NA = LP ? 4 : 8;  // A fragment loads per pair when not ALDS
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  static_assert(PMAX <= 5, "a wave's pairs span at most two 1024-blocks");
   select_chunk(limbs, sigma, y, b, K, N, y_dtype);
-  float tsc[4];
-  token_scales<NT, LP>(sigma, b, threadIdx.x & 63, tsc);
   const int64_t region = LP ? limb_region_bytes(b, K) : 32 * K;  // this chunk's limbs
   int8_t *lx = reinterpret_cast<int8_t *>(smem);
   char *ls = smem + (ALDS ? lds_limb_bytes : 0);
   const int G = int(K / kGroup);
-  float *red = reinterpret_cast<float *>(ls + scale_lds_bytes(16 * RB, G));
+  float *lsig = reinterpret_cast<float *>(ls + scale_lds_bytes(16 * RB, G));  // limb scales [b][nbk]
+  float *red = lsig + kSigLds / 4;
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar arithmetic
   const int col = lane & 15, qd = lane >> 4;
   const int GP = (G + 1) >> 1;
   const int64_t NB = (N + 15) >> 4;
-  const int p_begin = (GP * wave) / W;
-  const int np = (GP * (wave + 1)) / W - p_begin;
+  // the wave's pairs GP w / W .. GP (w + 1) / W - 1, divided by multiplying with
+  // wmagic = ceil(2^16 / W) (exact: GP (w + 1) < 4096 <= 2^16 / W)
+  const int p_begin = int((uint32_t(GP * wave) * wmagic) >> 16);
+  const int np = int((uint32_t(GP * (wave + 1)) * wmagic) >> 16) - p_begin;
   const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
+  // The wave's pairs lie in 1024-block fb and, from pair 4 lb on, in block lb
+  // (four pairs a block, at most five pairs a wave, so at most two blocks).  The
+  // sums of each block are kept apart and scaled by that block's limb scales at
+  // the end; the scales come into LDS with the other direct loads, so no load
+  // of the weight stream waits for them.  Only the variants with limbs in LDS
+  // have the registers for a second set of sums; the plan gives the others only
+  // shapes whose waves' pairs stay in one block.
+  const int nbk = limb_blocks(K);
+  const int fb = min(p_begin >> 2, nbk - 1), lb = min((p_begin + np - 1) >> 2, nbk - 1);
 
   // A operand row of this lane: (token, limb) per the LP or two-limb mapping
   const int tok = LP ? lp_token(col) : token_of_arow(col);
@@ -422,6 +437,13 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
 
   // 1. direct loads into LDS
   stage_scales(scales, N, G, n0, 16 * RB, ls, wave, W, lane);
+  if (wave == W - 1) {
+    // the chunk's b x nbk limb scales in 16-byte pieces (the workspace holds those
+    // of 64 tokens, so a rounded-up last piece stays inside it)
+    const int pieces = (b * nbk * 4 + 15) >> 4;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char *>(sigma) + 16 * min(lane, pieces - 1),
+                                     (__attribute__((address_space(3))) void *)lsig, 16, 0, 0);
+  }
   if (ALDS) {
     for (int blk = wave; blk * 1024 < lds_limb_bytes; blk += W) {
       const int64_t off = int64_t(blk) * 1024 + 16 * lane;
@@ -454,16 +476,21 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
       wv[pi][rb] = load_tile(packed, min(int64_t(blockIdx.x) * RB + rb, NB - 1), GP, p, lane);
   }
   asm volatile("" ::: "memory");
-  // 3. wait for the direct loads only; the register loads may stay in flight
+  // 3. wait for the direct loads only; the register loads may stay in
+  //    flight.  With limbs in LDS nothing may be scheduled above this point: work
+  //    on a tile moved up here would make the wait cover every load (the counter
+  //    is in order).  With limbs in registers the compiler's own interleaving of
+  //    the first pairs' matrix instructions with the loads is the faster one.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm<PMAX * (RB + (ALDS ? 0 : NA))>());
   __builtin_amdgcn_s_barrier();
+  if constexpr (ALDS) __builtin_amdgcn_sched_barrier(0);
 
   // 4. pairs in arrival order.  LDS is read through lds_read* so that the
   //    compiler, which cannot tell these reads from the destinations of the
   //    direct loads, does not make each of them wait for every register load.
   //    The next pair's LDS reads are issued before this pair's matrix
   //    instructions (two register slots), so their latency overlaps the work.
-  float acc[RB][4];
+  float acc[RB][4], acc1[ALDS ? RB : 1][4];  // acc1: block fb's sums once block lb starts
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -515,7 +542,34 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
       sv[0][rb] = live ? half_bits_to_float(uint16_t(sbs[sl][0][rb])) : 0.0f;
       sv[1][rb] = live && 2 * p + 1 < G ? half_bits_to_float(uint16_t(sbs[sl][1][rb])) : 0.0f;
     }
+    if constexpr (ALDS) {
+      if (lb != fb && live && p == 4 * lb) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc1[rb][i] = acc[rb][i], acc[rb][i] = 0.0f;
+      }
+    }
     pair_mfma<RB, NT, LP>(ah, al, wv[pi], sv, acc);
+  }
+  // each block's sums times its limb scales (and the 1/64 of the unpacked codes);
+  // every LDS read of the loop has been waited for
+  float ua[4], ub[ALDS ? 4 : 1];
+  token_scales<NT, LP>(lsig + fb, nbk, b, lane, ua);
+  if constexpr (ALDS) token_scales<NT, LP>(lsig + lb, nbk, b, lane, ub);
+  float tsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tsc[i] = 1.0f / 64.0f;
+  if (ALDS && lb != fb) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[rb][i] = acc1[ALDS ? rb : 0][i] * ua[i] + acc[rb][i] * ub[ALDS ? i : 0];
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < NT; ++i) acc[rb][i] *= ua[i];
   }
   __syncthreads();  // every wave is done with LDS before `red` is written
   reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
@@ -564,7 +618,7 @@ __global__ __launch_bounds__(q8_heavy(ALDS, RB, PMAX) ? 512 : 1024) void gemv_q8
   float *red = reinterpret_cast<float *>(ls + scale_lds_bytes(16 * RB, G));
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar arithmetic
   const int col = lane & 15, qd = lane >> 4;
   const int GP = (G + 1) >> 1;
   const int64_t NB = (N + 15) >> 4;
@@ -658,7 +712,9 @@ __global__ __launch_bounds__(q8_heavy(ALDS, RB, PMAX) ? 512 : 1024) void gemv_q8
   }
   __syncthreads();  // every wave is done with LDS before `red` is written
   float tsc[4];
-  token_scales<NT, false>(tok_scale, b, lane, tsc);
+  token_scales<NT, false>(tok_scale, 1, b, lane, tsc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tsc[i] *= 1.0f / 64.0f;
   reduce_and_store<RB, NT, false>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
 }
 
@@ -703,6 +759,18 @@ struct GemvWaveCap {
   static constexpr int value = RB == 1 ? 12 : RB == 2 ? 8 : 4;
 };
 
+// before pair q: where a 1024-block starts, the sums change to its units (the
+// chunk's limb scales lsig [b][nbk] are in LDS)
+template <int RB, int NT, bool LP>
+__device__ __forceinline__ void ring_block(int q, int &cb, float (&acc)[RB][4], float (&ua)[4],
+                                           const float *lsig, int nbk, int b, int lane) {
+  if ((q >> 2) == cb) return;
+  cb = q >> 2;
+  float un[4];
+  token_scales<NT, LP>(lsig + cb, nbk, b, lane, un);
+  change_units<RB, NT>(acc, ua, un);
+}
+
 template <int RB, int NT, bool LP>
 __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
     const int8_t *__restrict__ limbs, const float *__restrict__ sigma, int b, int64_t K,
@@ -710,10 +778,11 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
     void *__restrict__ y, int y_dtype) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   select_chunk(limbs, sigma, y, b, K, N, y_dtype);
-  float tsc[4];
-  token_scales<NT, LP>(sigma, b, threadIdx.x & 63, tsc);
-  char *ls = smem;  // scale block of the workgroup's rows, then (W - 1) * RB * NT * 64 floats
-  float *red = reinterpret_cast<float *>(smem + scale_lds_bytes(16 * RB, int(K / kGroup)));
+  // scale block of the workgroup's rows, the chunk's limb scales [b][nbk], then
+  // (W - 1) * RB * NT * 64 floats
+  char *ls = smem;
+  float *lsig = reinterpret_cast<float *>(smem + scale_lds_bytes(16 * RB, int(K / kGroup)));
+  float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(lsig) + ring_sig_bytes(K));
   const int W = blockDim.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -724,6 +793,11 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
   const int p_begin = (GP * wave) / W;
   const int p_end = (GP * (wave + 1)) / W;
   const int64_t n0 = int64_t(blockIdx.x) * (16 * RB);
+  // the sums hold units of the limb scale of block cb and change units as each
+  // next 1024-block starts (four pairs a block), with the scales from LDS
+  const int nbk = limb_blocks(K);
+  int cb = min(p_begin >> 2, nbk - 1);
+  for (int e = threadIdx.x; e < b * nbk; e += blockDim.x) lsig[e] = sigma[e];
 
   const int tok = LP ? lp_token(col) : token_of_arow(col);
   const int tok_ld = tok < b ? tok : b - 1;
@@ -746,17 +820,24 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
   stage_scales(scales, N, G, n0, 16 * RB, ls, wave, W, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  float ua[4];
+  token_scales<NT, LP>(lsig + cb, nbk, b, lane, ua);
   for (int p = p_begin; p < p_end; p += 2) {
     float s[2][RB];
     pair_scales<RB>(s, ls, col, G, p);
+    ring_block<RB, NT, LP>(p, cb, acc, ua, lsig, nbk, b, lane);
     pair_mfma<RB, NT, LP>(sl[0].ah, LP ? sl[0].ah : sl[0].al, sl[0].w, s, acc);
     if (p + 2 < p_end) load_pair<RB, LP>(sl[0], p + 2, G, GP, ah, al, packed, rbg, lane);
     if (p + 1 < p_end) {
       pair_scales<RB>(s, ls, col, G, p + 1);
+      ring_block<RB, NT, LP>(p + 1, cb, acc, ua, lsig, nbk, b, lane);
       pair_mfma<RB, NT, LP>(sl[1].ah, LP ? sl[1].ah : sl[1].al, sl[1].w, s, acc);
       if (p + 3 < p_end) load_pair<RB, LP>(sl[1], p + 3, G, GP, ah, al, packed, rbg, lane);
     }
   }
+  float tsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tsc[i] = ua[i] * (1.0f / 64.0f);
   reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
 }
 
@@ -818,6 +899,16 @@ const char *variant_name(int kind, int rb, int waves, int pmax) {
   return table[((size_t(kind) * 4 + (rb - 1)) * 17 + waves) * (kPmaxLds + 1) + pmax].c_str();
 }
 
+// true when some wave's share of the GP pairs (GP w / W .. GP (w + 1) / W - 1)
+// reaches across a 1024-block boundary (four pairs)
+bool straddles(int64_t GP, int W) {
+  for (int w = 0; w < W; ++w) {
+    const int64_t pb = GP * w / W, pe = GP * (w + 1) / W - 1;
+    if (pe >= pb && (pb >> 2) != (pe >> 2)) return true;
+  }
+  return false;
+}
+
 GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   // more than 16 tokens: one grid row per chunk of 16, each shaped like b = 16
   const int64_t chunks = b > kTokChunk ? limb_chunks(b) : 1;
@@ -827,7 +918,6 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   const int64_t limb_bytes = (limb_region_bytes(b, K) + 1023) / 1024 * 1024;
   GemvPlan p{};
   const bool lp = b <= 8;
-  // waves for PMAX pairs each, within the wave cap of the resulting variant
   // waves for PMAX pairs each, within the wave cap of the resulting variant; false
   // when even the largest pair count leaves more waves than the cap allows
   auto shape = [&](bool alds, int rb, int pmax) {
@@ -842,7 +932,8 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
       if (pmax >= (alds ? kPmaxLds : kPmaxReg)) return false;
     }
   };
-  // Row blocks per workgroup, 1..4: the smallest whose workgroups are all resident
+  // Row blocks per workgroup, 1..4 (limbs in LDS: the measured rule below first):
+  // the smallest whose workgroups are all resident
   // at once (one round), else the one with the lowest rounds x (3 + RB).  A
   // workgroup costs about 3 row blocks' worth of weight streaming for its fixed
   // part (limbs, scales, reduction) plus one per row block: the fit to measured qkv
@@ -852,11 +943,28 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
   // Row blocks that cannot be shaped, or whose LDS exceeds the compute unit's, are
   // skipped; 0 when none is left.
   auto choose_rb = [&](bool alds, int pmax0, size_t lds_limbs) {
+    if (alds) {
+      // limbs in LDS: the row-block count measured best (qkv 5120 -> 10240, o
+      // 5120 -> 5120, gate_up 5120 -> 34816 and a 1024 -> 300 layer at
+      // b = 1, 2, 4, 8; each workgroup stages 2 b K bytes of limbs): one row block
+      // while b <= 2, while b <= 4 and the grid of single row blocks is at most
+      // three per CU, or when it does not even fill the CUs; else three, or two
+      // where three would leave a quarter of the CUs idle.  (gate_up b = 1:
+      // 11.2 us at one against 13.0 at two; qkv b = 8: 6.9 us at three against
+      // 9.0 at two and 9.8 at one; o b = 8: 5.3 us at two against 6.4 at three.)
+      const int64_t rows16 = (N + 15) / 16 * chunks, rows48 = (N + 47) / 48 * chunks;
+      const int pref = rows16 <= kCUs || b <= 2 || (b <= 4 && rows16 <= 3 * kCUs) ? 1
+                       : rows48 >= 3 * kCUs / 4 ? 3 : 2;
+      const size_t lds = lds_limbs + scale_lds_bytes(16 * pref, int(G)) + kSigLds;
+      if (shape(true, pref, pmax0) &&
+          lds + size_t(p.waves > 1 ? p.waves - 1 : 1) * pref * nt * 256 <= size_t(kLdsPerCU))
+        return pref;
+    }
     int best = 0;
     int64_t best_cost = INT64_MAX;
     for (int rb = 1; rb <= 4; ++rb) {
-      if (!shape(alds, rb, pmax0)) continue;
-      const size_t lds = lds_limbs + scale_lds_bytes(16 * rb, int(G)) +
+      if (!shape(alds, rb, pmax0) || (!alds && straddles(GP, p.waves))) continue;
+      const size_t lds = lds_limbs + scale_lds_bytes(16 * rb, int(G)) + kSigLds +
                          size_t(p.waves > 1 ? p.waves - 1 : 1) * rb * nt * 256;
       if (lds > size_t(kLdsPerCU)) continue;
       int64_t per_cu = stream_resident(alds, rb, b, p.pmax, p.waves, lds);
@@ -864,6 +972,12 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
         const int wave_cap = stream_heavy(alds, rb, p.pmax, lp) ? 8 : 16;
         per_cu = std::max<int64_t>(1, std::min<int64_t>(int64_t(kLdsPerCU / lds), wave_cap / p.waves));
       }
+      // limbs from L2: every workgroup reads all b tokens' limbs itself (2 b K
+      // bytes, against 4 K of weights per row block), so a second workgroup on a
+      // compute unit adds that traffic rather than hiding latency: count one
+      // (b = 16 qkv: 3 row blocks in 213 workgroups 7.7 us, 2 in 320 resident
+      // two per CU 9.7 us)
+      if (!alds) per_cu = 1;
       const int64_t wgs = (N + 16 * rb - 1) / (16 * rb) * chunks;
       const int64_t rounds = (wgs + per_cu * kCUs - 1) / (per_cu * kCUs);
       if (rounds == 1) return rb;
@@ -882,7 +996,8 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     p.rb = rb;
     shape(true, p.rb, b <= 4 ? 5 : 3);
   } else if (GP <= 8 * kPmaxReg && (rb = choose_rb(false, 2, 0)) > 0) {
-    // limbs from L2 into registers, all pairs at once
+    // limbs from L2 into registers, all pairs at once (shapes whose waves' pairs
+    // each stay inside one 1024-block)
     p.kind = 1;
     p.lds_limb_bytes = 0;
     p.rb = rb;
@@ -895,11 +1010,12 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     p.pmax = 0;
     p.lds_limb_bytes = 0;
   }
-  p.lds_bytes = size_t(p.lds_limb_bytes) + scale_lds_bytes(16 * p.rb, int(G)) +
+  p.lds_bytes = size_t(p.lds_limb_bytes) + scale_lds_bytes(16 * p.rb, int(G)) + (p.kind == 2 ? ring_sig_bytes(K) : kSigLds) +
                 size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * nt * 64 * sizeof(float);
   p.name = variant_name(p.kind, p.rb, p.waves, p.pmax);
   p.chunks = int(chunks);
-  p.ok = p.lds_bytes <= size_t(kLdsPerCU) && p.waves >= 1 && 64 * p.waves <= 1024;
+  p.ok = p.lds_bytes <= size_t(kLdsPerCU) && p.waves >= 1 && 64 * p.waves <= 1024 &&
+         (p.kind == 2 || GP * p.waves < 4096);  // the stream kernels' reciprocal division
   return p;
 }
 
@@ -924,7 +1040,7 @@ void launch_stream_t(const GemvPlan &p, dim3 grid, const GemvArgs &a) {
   }
   hipLaunchKernelGGL((gemv_stream_kernel<RB, NT, PMAX, LP, ALDS>), grid, dim3(64 * p.waves), p.lds_bytes,
                      a.stream, a.w->xhi, a.w->sigma, int(a.b), a.K, a.w->Kp, a.N, a.packed, a.scales, a.y,
-                     a.y_dtype, p.lds_limb_bytes);
+                     a.y_dtype, p.lds_limb_bytes, (65536u + p.waves - 1) / p.waves);
 }
 
 template <int RB, int NT, bool LP, bool ALDS>
@@ -1243,8 +1359,9 @@ bool gemv_supported(int64_t b, int64_t K, int64_t N) {
 }
 
 size_t gemv_workspace_bytes(int64_t b, int64_t K, int64_t /*N*/) {
-  // two int8 limb planes [b, K + 16] and the per-token scales
-  return align256(size_t(limb_region_bytes(b, K))) + align256(size_t(kGemvMaxTokens) * sizeof(float));
+  // the two int8 limbs of b tokens, then the limb scales of up to 64 tokens
+  return align256(size_t(limb_region_bytes(b, K))) +
+         align256(size_t(kGemvMaxTokens) * limb_blocks(K) * sizeof(float));
 }
 
 namespace {
@@ -1279,8 +1396,8 @@ hipError_t launch_gemv_prepare(const float *xr, int64_t b, int64_t K, void *work
                                hipStream_t stream) {
   const GemvWs w = carve(workspace, b, K);
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  hipLaunchKernelGGL(gemv_prep_kernel, dim3(unsigned(b)), dim3(kPrepThreads), 0, stream, xr, K, w.Kp,
-                     int(b), w.xhi, w.sigma);
+  hipLaunchKernelGGL(gemv_prep_kernel, dim3(unsigned(b * limb_blocks(K))), dim3(64), 0, stream, xr, K,
+                     w.Kp, int(b), w.xhi, w.sigma);
   set_last_kernel("gemv_prep_limbs");
   return hipGetLastError();
 }

@@ -59,8 +59,12 @@ __device__ __forceinline__ void rotate_load(const uint16_t *__restrict__ xblk,
 }
 
 // Rotates one block from the lane's raw inputs (loaded by rotate_load; signs used
-// when `signed_in`).  On return out[j] = fl32(rotation[lane + 64 j]).  lds: kRotLds
-// doubles owned by the calling wavefront.
+// when `signed_in`).  On return out[j] = fl32(rotation[lane + 64 j]), or with RUNS
+// out[4 s + c] = fl32(rotation[256 s + 4 lane + c]): four runs of four consecutive
+// elements per lane, for 4-byte and 16-byte stores.  The butterfly stages along
+// different index bits commute and every partial sum is exact, so both layouts
+// hold the same values.  lds: kRotLds doubles owned by the calling wavefront.
+template <bool RUNS = false>
 __device__ __forceinline__ void rotate_block_raw(const RotRaw &r, bool signed_in, double *lds, int lane,
                                                  float (&out)[kRotEPT]) {
   // phase A: lane owns elements 16*lane + j
@@ -101,9 +105,12 @@ __device__ __forceinline__ void rotate_block_raw(const RotRaw &r, bool signed_in
   for (int j = 0; j < kRotEPT; ++j) lds[rot_lds_pad(ib | (j << 4))] = v[j];  // the slots it read
   rot_wave_sync();
 
-  // phase C: element lane + 64 j; slot bits 2-3 are index bits 8-9
+  // phase C: slot bits 2-3 are index bits 8-9; the other index bits are the lane's
+  // (element lane + 64 j) or, with RUNS, lane bits 0-5 are index bits 2-7 and slot
+  // bits 0-1 index bits 0-1 (element 256 (j / 4) + 4 lane + j % 4)
 #pragma unroll
-  for (int j = 0; j < kRotEPT; ++j) v[j] = lds[rot_lds_pad(lane + 64 * j)];
+  for (int j = 0; j < kRotEPT; ++j)
+    v[j] = lds[rot_lds_pad(RUNS ? (j & 3) | (lane << 2) | ((j >> 2) << 8) : lane + 64 * j)];
   rot_stage<4>(v);
   rot_stage<8>(v);
 #pragma unroll

@@ -55,4 +55,49 @@ __device__ __forceinline__ float block_max(float v, float *red /* NT/64 floats *
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// decode activation limbs
+constexpr float kLimbRange = 32639.0f;  // 127 * 257: hi, lo of 256*hi + lo stay in int8
+
+// The two int8 limbs of one 1024-block of token t, held by a wavefront in runs:
+// v[4 s + c] is element k0 + 256 s + 4 lane + c (elements at or past len, a
+// multiple of 128, are ignored).  The block's scale sigma = |v|max / 32639 goes
+// to *sig; each value becomes q = clamp(RNE(fl32(v * fl32(32639 / |v|max))),
+// +-32639) = 256 hi + lo with hi = floor((q + 128) / 256), so that lo lies in
+// [-128, 127].  A run of four elements is one 4-byte store per limb, in the
+// limb layout of the workspace (rows for b <= 8, operand order above).
+__device__ __forceinline__ void store_block_limbs(const float (&v)[16], int lane, int t, int b, int64_t K,
+                                                  int64_t Kp, int64_t k0, int len, int8_t *__restrict__ xhi,
+                                                  float *__restrict__ sig) {
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (256 * (j >> 2) + 4 * lane < len) m = fmaxf(m, fabsf(v[j]));
+  m = wave_max(m);
+  if (lane == 0) *sig = m / kLimbRange;
+  const float inv = m > 0.0f ? kLimbRange / m : 0.0f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int e = 256 * s + 4 * lane;
+    if (e >= len) continue;
+    uint32_t h = 0, l = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int q = (int)rintf(v[4 * s + c] * inv);
+      q = q > 32639 ? 32639 : (q < -32639 ? -32639 : q);
+      const int hi = (q + 128) >> 8;
+      h |= uint32_t(hi & 0xFF) << (8 * c);
+      l |= uint32_t((q - 256 * hi) & 0xFF) << (8 * c);
+    }
+    const int64_t k = k0 + e;
+    if (b > 8) {
+      *reinterpret_cast<uint32_t *>(xhi + limb_frag_offset(t, k, 0, K)) = h;
+      *reinterpret_cast<uint32_t *>(xhi + limb_frag_offset(t, k, 1, K)) = l;
+    } else {
+      *reinterpret_cast<uint32_t *>(xhi + int64_t(t) * Kp + k) = h;
+      *reinterpret_cast<uint32_t *>(xhi + (int64_t(b) + t) * Kp + k) = l;
+    }
+  }
+}
+
 }  // namespace tl

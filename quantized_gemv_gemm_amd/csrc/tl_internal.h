@@ -33,10 +33,13 @@ hipError_t launch_quant(const float *xr, int64_t T, int64_t K, int8_t *xq, float
 // chunk, for group g, 64-k half h and limb l, 64 lanes x 16 bytes, where lane
 // r + 16 q holds A row r (token 16 c + 4 (r % 4) + r / 4) and
 // k = 128 g + 32 q + 16 h + j.
+// Limb scales: sigma[t][j] = |x|max / 32639 of token t's 1024-block j (the last
+// block may be shorter), limb_blocks(K) per token, after the limbs.
 constexpr int kLimbRowPad = 16;
 constexpr int kTokChunk = 16;      // tokens per MFMA operand (and per GEMV grid row)
 constexpr int kGemvMaxTokens = 64; // decode tokens per call
 __host__ __device__ inline int64_t limb_chunks(int64_t b) { return (b + kTokChunk - 1) / kTokChunk; }
+__host__ __device__ inline int limb_blocks(int64_t K) { return int((K + kHBlock - 1) / kHBlock); }
 __host__ __device__ inline int64_t limb_region_bytes(int64_t b, int64_t K) {
   return b > 8 ? 32 * K * limb_chunks(b) : 2 * b * (K + kLimbRowPad);
 }

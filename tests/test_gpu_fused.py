@@ -29,7 +29,7 @@ def _limb_region(b, K):
 
 
 def _limbs(ws, b, K):
-    """hi and lo limb rows [b, K] and the token scales from a GEMV workspace: rows
+    """hi and lo limb rows [b, K] and the limb scales [b, K/1024] from a GEMV workspace: rows
     K + 16 bytes apart for b <= 8; for b > 8 the matrix-core operand order (chunks
     of 16 tokens 32 K bytes apart; in a chunk, per 128-group, 64-k half and limb:
     64 lanes x 16 bytes, lane = row + 16 (k%128)//32, row = 4 (t % 4) + (t % 16) // 4)."""
@@ -49,7 +49,21 @@ def _limbs(ws, b, K):
             hi[t] = a[base]
             lo[t] = a[base + 64 * 16]
     off = (_limb_region(b, K) + 255) // 256 * 256
-    return hi, lo, a[off:off + 4 * b].view(np.float32)
+    nbk = (K + 1023) // 1024
+    return hi, lo, a[off:off + 4 * b * nbk].view(np.float32).reshape(b, nbk)
+
+
+def _expected_limbs(xr):
+    """The limb split of f32 rows xr [b, K] (K % 1024 == 0), per token and 1024-block:
+    sigma = |x|max / 32639 and q = clamp(RNE(fl32(x * fl32(32639 / |x|max))), +-32639),
+    every step in binary32 as the kernels take it (q decides integers)."""
+    b, K = xr.shape
+    blk = xr.reshape(b, K // 1024, 1024)
+    amax = np.abs(blk).max(axis=2)
+    sigma = (amax / np.float32(32639.0)).astype(np.float32)
+    inv = np.where(amax > 0, np.float32(32639.0) / np.where(amax > 0, amax, np.float32(1)), 0).astype(np.float32)
+    q = np.rint((blk * inv[..., None]).astype(np.float32)).clip(-32639, 32639).astype(np.int32)
+    return sigma, q.reshape(b, K)
 
 
 @pytest.mark.parametrize("K,b,signed", [(1024, 1, False), (5120, 4, True), (5120, 16, False),
@@ -73,11 +87,12 @@ def test_gemv_prepare_fused_bitexact(tl, K, b, signed):
     np.testing.assert_array_equal(h1, h0)
     np.testing.assert_array_equal(l1, l0)
     np.testing.assert_array_equal(s1, s0)
-    # the limbs are the oracle's fixed-point split of the f32 rotation
+    # the limbs are the fixed-point split of the oracle's f32 rotation, per 1024-block
     xr = oracle.rotate_f32(synth.bf16_bits_to_f32(xbits), _signs(K, K + b) if signed else None)
-    amax = np.abs(xr).max(axis=1)
-    np.testing.assert_array_equal(s0, (amax / np.float32(32639.0)).astype(np.float32))
+    sigma, q = _expected_limbs(xr)
+    np.testing.assert_array_equal(s0, sigma)
     v = h0.astype(np.int8).astype(np.int32) * 256 + l0.astype(np.int8).astype(np.int32)
+    np.testing.assert_array_equal(v, q)
     assert np.abs(v).max() <= 32639
 
 
@@ -104,8 +119,8 @@ def test_gemv_ternary_fused_matches(tl, K, N, b):
 
 def _check_fused_vs_sequence(tl, y_fus, y_seq):
     """The prep + GEMV pair is bit-identical to the rotation kernel + GEMV; the
-    one-launch kernel (one or two tokens) scales its limbs per 1024-block instead
-    of per token, so it differs from them by the rounding of the limbs alone:
+    one-launch kernel (one or two tokens) has the same limbs but adds the groups'
+    results in another order, so it differs from them by float rounding alone:
     both lie within about 3e-5 of the exact layer."""
     kname = tl.last_kernel_name()
     if kname.startswith("gemv_rot"):

@@ -237,6 +237,42 @@ def test_gemv_ragged(tl, K, N, b):
         assert oracle.rel_fro(got[t], ref[t]) <= REL_TOL
 
 
+@pytest.mark.parametrize("K,N,b", [(5120, 300, 4), (5120, 300, 16), (2304, 1000, 16), (17408, 200, 1),
+                                   (17408, 200, 16), (3200, 64, 8)])
+def test_gemv_block_scales(tl, K, N, b):
+    """Activations whose 1024-blocks differ wildly in size: a block of zeros
+    (first, middle, last), a block 1e-6 times and one 1e3 times the rest.  The
+    limbs are scaled per block, and a wave whose pairs span two blocks changes the
+    units of its sums once (in every kernel shape: limbs in LDS or registers, or
+    the long-K ring)."""
+    import torch
+    d = dev()
+    rng = np.random.default_rng(K * 7 + b)
+    codes = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scales = np.exp(-4 + 0.5 * rng.standard_normal((N, K // 128))).astype(np.float16)
+    xr = rng.standard_normal((b, K)).astype(np.float32)
+    nbk = (K + 1023) // 1024
+    for t in range(b):
+        j = t % nbk
+        kind = t % 4
+        sl = slice(1024 * j, min(K, 1024 * (j + 1)))
+        if kind == 0:
+            xr[t, sl] = 0
+        elif kind == 1:
+            xr[t, sl] *= 1e-6
+        elif kind == 2:
+            xr[t, sl] *= 1e3
+    packed, _, _ = tl.pack_weights(to_dev(codes, d), to_dev(scales, d))
+    y = poison_(torch.empty((b, N), dtype=torch.float32, device=d))
+    announce(f"tl_gemv_ternary block scales K={K} N={N} b={b}")
+    tl.gemv_ternary(to_dev(xr, d), packed, to_dev(scales, d), out=y)
+    announce(f"  kernel={tl.last_kernel_name()}")
+    got = y.cpu().numpy()
+    ref = oracle.gemv_ternary(xr, codes, scales)
+    for t in range(b):
+        assert oracle.rel_fro(got[t], ref[t]) <= REL_TOL, t
+
+
 def test_gemv_zero_token(tl):
     d = dev()
     L = layer("tiny", tl)
