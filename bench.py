@@ -113,7 +113,7 @@ def _attribute(rows):
 
     Launches are attributed by their order inside a step: DEC_LAYERS GEMV launches
     for each b in DECODE_BS, then PRE_LAYERS GEMM launches for gate_up and for down.
-    The GEMV launches of the launch-cost fit follow the steps and are dropped."""
+    The GEMV launches of the read-floor comparison follow the steps and are dropped."""
     gemv = [(n, v) for n, v in rows if "gemv_stream_kernel" in n or "gemv_ring_kernel" in n]
     gemm = [(n, v) for n, v in rows if "gemm_i8_kernel" in n]
     gemv = gemv[:len(gemm) // (2 * PRE_LAYERS) * DEC_LAYERS * len(DECODE_BS)]
@@ -205,6 +205,11 @@ def roofline_gate(out):
     rc = out["launch_floor"].get("read_codes")
     if rc and rc["GBps"] > HBM_PEAK_GBS:
         bad.append(f"read floor {rc['GBps']} GB/s")
+    for b, rows in out.get("gemv_vs_read_floor", {}).items():
+        for r in rows:
+            for key in ("gemv_GBps", "read_GBps"):
+                if r[key] > HBM_PEAK_GBS:
+                    bad.append(f"gemv_vs_read_floor {b} {r['shape']} {key} {r[key]}")
     st = out.get("stack64")
     if st:
         if st["decode_b16"]["gemv_GBps"] > HBM_PEAK_GBS:
@@ -407,16 +412,26 @@ def main():
     prep_ms = {b: [run_time(lambda: tl.gemv_prepare_x(x_dec[b], ws_dec[b]))] for b in DECODE_BS}
     quant_ms = {k: [run_time(lambda: tl.quant_act_int8_x(P["x"], xq=P["xq"], tok_scale=P["sx"]))]
                 for k, P in pre.items()}
-    # Launch-cost fit of the GEMV weight stream, t = F + bytes / BW, over the three
-    # layer shapes (qkv, down, gate_up: 14 to 48 MB) at b = 1 and 16, each the mean of
-    # DEC_LAYERS back-to-back launches over rotating weight copies behind a spin:
-    # F is the fixed per-launch cost, BW the rate at which the kernel streams.
-    fit = {}
-    fit_shapes = (("qkv", qkv, 5120, 10240), ("down", pre["down"]["copies"], 17408, 5120),
-                  ("gate_up", pre["gate_up"]["copies"], 5120, 34816))
+    # The GEMV weight stream against the streaming floor, per layer shape (qkv,
+    # down, gate_up: 14 to 48 MB) at b = 1 and 16: the GEMV's time and that of a
+    # launch that only reads the same layer's packed codes (read_probe), each the
+    # mean of back-to-back launches over rotating weight copies behind a spin.
+    # excess_us = what the GEMV adds on top of moving its codes at all.
+    sink_f = torch.zeros((4,), dtype=torch.int32, device=dev)
+    vs_floor = {}
+    floor_shapes = (("qkv", qkv, 5120, 10240), ("down", pre["down"]["copies"], 17408, 5120),
+                    ("gate_up", pre["gate_up"]["copies"], 5120, 34816))
+    read_us = {}
+    for name, copies, K, N in floor_shapes:
+        kr = [0]
+
+        def read_one():
+            tl.read_probe(copies[kr[0] % len(copies)][0], sink_f)
+            kr[0] += 1
+        read_us[name] = run_time(read_one, n=DEC_LAYERS * 4) * 1e3
     for b in (1, 16):
-        pts = []
-        for name, copies, K, N in fit_shapes:
+        rows = []
+        for name, copies, K, N in floor_shapes:
             xr = tl.hadamard_blk(bf16(synth.activations(0, 2, 7, b, K)))
             ws = torch.empty((tl.gemv_workspace_size(b, K, N),), dtype=torch.uint8, device=dev)
             yb = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
@@ -428,15 +443,14 @@ def main():
                 k[0] += 1
                 tl.gemv_prepared(ws, b, K, packed, scales, yb)
             t_us = run_time(one, n=DEC_LAYERS * 4) * 1e3
-            pts.append((gemv_bytes(b, K, N), t_us, name, tl.last_kernel_name()))
-        xs = np.array([p[0] for p in pts], dtype=np.float64)
-        ts = np.array([p[1] for p in pts], dtype=np.float64)
-        slope, icpt = np.polyfit(xs, ts, 1)          # µs per byte, µs
-        bw = 1e-3 / slope                            # GB/s
-        fit[f"b{b}"] = {"F_us": round(float(icpt), 2), "BW_GBps": round(float(bw), 1),
-                        "BW_frac": round(float(bw) / HBM_PEAK_GBS, 4),
-                        "points": [{"shape": n, "bytes": int(x), "us": round(t, 2), "kernel": kn}
-                                   for x, t, n, kn in pts]}
+            code_bytes = copies[0][0].numel() * 4
+            rows.append({"shape": name, "kernel": tl.last_kernel_name(), "gemv_us": round(t_us, 2),
+                         "gemv_bytes": int(gemv_bytes(b, K, N)),
+                         "gemv_GBps": round(gemv_bytes(b, K, N) / (t_us * 1e-6) / 1e9, 1),
+                         "read_codes_us": round(read_us[name], 2), "code_bytes": int(code_bytes),
+                         "read_GBps": round(code_bytes / (read_us[name] * 1e-6) / 1e9, 1),
+                         "ratio": round(t_us / read_us[name], 3), "excess_us": round(t_us - read_us[name], 2)})
+        vs_floor[f"b{b}"] = rows
     # the rotation alone (tl_hadamard_blk: bf16 in, f32 out), at the decode and prefill sizes
     rot_only = {}
     for label, xs in (("decode_b16_k5120", x_dec[16]), ("prefill_m512_k17408", pre["down"]["x"])):
@@ -568,7 +582,7 @@ def main():
                    "decode_b": list(DECODE_BS), "prefill_tokens": PREFILL_M,
                    "rotating_weight_bytes": ROTATE_BYTES},
         "decode_gemv_by_b": by_b,
-        "gemv_launch_fit": fit,
+        "gemv_vs_read_floor": vs_floor,
         "rotation_only": rot_only,
         "input_kernels_GBps": {
             "decode_rotate_prep": {str(b): round((2 * b * Kq + 2 * b * Kq + 4 * b) / (float(np.mean(prep_ms[b])) * 1e-3) / 1e9, 1)
