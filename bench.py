@@ -74,6 +74,9 @@ def parse():
                         "shapes, with int8 weights already expanded, beside this library's GEMM")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
+    p.add_argument("--phase-stamps", action="store_true",
+                   help="load the instrumented library (python -m quantized_gemv_gemm_amd._build --phase-stamps) "
+                        "and print the decode GEMV's per-wave phase times at qkv and gate_up, b = 1, 4, 8, 16")
     p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                    help="print the per-launch median of every counter in rocprofv3 --pmc CSVs of this bench "
                         "(--steps S --warmup W), one row per decode b and prefill shape, then exit")
@@ -248,6 +251,11 @@ def main():
     import quantized_gemv_gemm_amd as tl
     import synth
 
+    if args.phase_stamps:
+        from quantized_gemv_gemm_amd import _build
+        if not os.path.exists(_build.STAMPS_LIB):
+            raise SystemExit(f"{_build.STAMPS_LIB} is not built: python -m quantized_gemv_gemm_amd._build --phase-stamps")
+        tl.LIB_PATH = _build.STAMPS_LIB
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tl.lib()
@@ -295,6 +303,10 @@ def main():
     # ---------------- activations ----------------
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    if args.phase_stamps:
+        phase_stamps(tl, torch, dev, {"qkv": (qkv, 5120, 10240), "gate_up": (gate_up, 5120, 34816)}, bf16, synth)
+        return
 
     Kq, Nq = 5120, 10240
     x_dec = {b: bf16(synth.activations(0, 1, 0, b, Kq)) for b in DECODE_BS}
@@ -846,6 +858,68 @@ def stack_pass(tl, torch, dev, steps, log):
         log(f"stack64 {name}: {out[name]}")
     gc.enable()
     return out
+
+
+PHASES = ("issue", "direct_wait", "barrier", "first_pair", "other_pairs", "to_reduction")
+
+
+def phase_stamps(tl, torch, dev, layers, bf16, synth):
+    """Per-wave phase times of the decode GEMV from the instrumented library.
+
+    Each launch group is DEC_LAYERS back-to-back launches over rotating weight
+    copies behind a device spin; every launch writes its waves' records (8 words
+    each, see the kernel) and those of the last launch remain and are read.  Phases per wave, in µs:
+    entry -> every load issued -> direct loads waited for -> barrier passed ->
+    first pair computed -> last pair computed -> stamps stored (the reduction
+    follows); plus the spread of entries and of the waves' output stores (each
+    wave adds and stores its share of the workgroup's outputs) across the grid.  The clock is the 100 MHz constant-rate counter."""
+    import ctypes
+    L = tl.lib()
+    L.tl_phase_stamps_set.argtypes = [ctypes.c_void_p]
+    L.tl_phase_stamps_set.restype = ctypes.c_int
+    buf = torch.zeros((4 * 4096 * 16 * 8,), dtype=torch.int64, device=dev)
+    out = {}
+    for name, (copies, K, N) in layers.items():
+        for b in DECODE_BS:
+            x = bf16(synth.activations(0, 1, 0, b, K))
+            ws = torch.empty((tl.gemv_workspace_size(b, K, N),), dtype=torch.uint8, device=dev)
+            y = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
+            tl.gemv_prepare_x(x, ws)
+            times, recs = [], []
+            for rep in range(5):
+                buf.zero_()
+                torch.cuda.synchronize()
+                assert L.tl_phase_stamps_set(ctypes.c_void_p(buf.data_ptr())) == 0
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(2_000_000)
+                e0.record()
+                for i in range(DEC_LAYERS):   # every launch writes the records; the last one's remain
+                    p, s = copies[(rep * DEC_LAYERS + i) % len(copies)][:2]
+                    tl.gemv_prepared(ws, b, K, p, s, y)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) * 1e3 / DEC_LAYERS)
+                a = buf.view(-1, 8).cpu().numpy()
+                recs.append(a[a[:, 0] > 0])
+            kname = tl.last_kernel_name()
+            a = recs[-1]
+            t0 = a[:, 0].min()
+            t = (a[:, :7].astype(np.float64) - t0) / 100.0           # µs from the first wave's entry
+            dur = np.diff(t[:, :6], axis=1)                             # five phases per wave
+            tail = t[:, 5]                                              # stamps stored: reduction starts
+            w0 = t[:, 6][a[:, 6] > 0]                                   # each wave: its outputs stored
+            xcc = ((a[:, 7] >> 32) & 0xF).astype(np.int64)
+            out[f"{name}_b{b}"] = {
+                "kernel": kname, "event_us": round(float(np.median(times)), 2), "waves": int(len(a)),
+                "phase_median_us": {ph: round(float(np.median(dur[:, k])), 2) for k, ph in enumerate(PHASES[:5])},
+                "entry_p10_p50_p90": [round(float(np.percentile(t[:, 0], q)), 2) for q in (10, 50, 90)],
+                "reduction_start_p10_p50_p90": [round(float(np.percentile(tail, q)), 2) for q in (10, 50, 90)],
+                "outputs_stored_p50_p90_max": [round(float(np.percentile(w0, q)), 2) for q in (50, 90)] +
+                                              [round(float(w0.max()), 2)],
+                "waves_per_xcd": np.bincount(xcc, minlength=8).tolist()}
+            print(f"[stamps] {name} b={b} {kname}: {out[f'{name}_b{b}']}", file=sys.stderr, flush=True)
+    assert L.tl_phase_stamps_set(ctypes.c_void_p(0)) == 0
+    print(json.dumps({"phase_stamps": out}))
 
 
 def host_info():

@@ -55,12 +55,13 @@ def _resources(remarks: str) -> dict:
     return out
 
 
-def _compile(src: str):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    flags = [f"-D{d}" for d in defines]
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, *flags, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     else:
-        cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *flags, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -107,5 +108,32 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+STAMPS_DIR = os.path.join(BUILD, "stamps")             # its objects
+STAMPS_LIB = os.path.join(PKG, "libtl_stamps.so")      # beside libtl.so, so that it travels with it
+
+
+def build_stamps(verbose: bool = False) -> str:
+    """The same library with the decode GEMV's phase timestamps compiled in
+    (TL_PHASE_STAMPS=1, adds tl_phase_stamps_set), for `bench.py --phase-stamps`
+    only; never loaded by the package."""
+    os.makedirs(STAMPS_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = [o for o, _ in ex.map(lambda s: _compile(s, STAMPS_DIR, ("TL_PHASE_STAMPS=1",)), srcs)]
+    tmp = STAMPS_LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, STAMPS_LIB)
+    if verbose:
+        print(f"built {STAMPS_LIB}")
+    return STAMPS_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys
+    if "--phase-stamps" in sys.argv:
+        build_stamps(verbose=True)
+    else:
+        build(verbose=True)

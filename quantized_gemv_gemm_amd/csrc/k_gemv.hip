@@ -320,48 +320,98 @@ __device__ __forceinline__ void change_units(float (&acc)[RB][4], float (&ua)[4]
   for (int i = 0; i < NT; ++i) change_unit<RB>(acc, i, ua[i], ub[i]);
 }
 
-// each wave's partial sums times its own token scales tsc (the limb or token
-// scale and the 1/64 of the unpacked codes) -> LDS -> wave 0 adds them and stores
+// output element of accumulator (rb, i) of the lane: token 2 qd + i (LP) or 4 i + qd, row 16 rb + col
+template <bool LP>
+__device__ __forceinline__ void store_out(float v, int rb, int i, int lane, int b, int64_t n0, int64_t N,
+                                          void *y, int y_dtype) {
+  const int col = lane & 15, qd = lane >> 4;
+  const int t = LP ? 2 * qd + i : 4 * i + qd;
+  const int64_t n = n0 + 16 * rb + col;
+  if (t >= b || n >= N) return;
+  if (y_dtype == TL_F32)
+    reinterpret_cast<float *>(y)[int64_t(t) * N + n] = v;
+  else
+    reinterpret_cast<uint16_t *>(y)[int64_t(t) * N + n] = float_to_bf16_bits(v);
+}
+
+// Each wave's partial sums times its own token scales tsc (the limb or token
+// scale and the 1/64 of the unpacked codes) go to LDS (W x RB x NT x 64 floats);
+// then accumulator c = rb NT + i of every lane is added over the waves, in wave
+// order, and stored by wave c mod W, so that the adds and stores are spread over
+// the waves instead of falling on one.
 template <int RB, int NT, bool LP>
 __device__ __forceinline__ void reduce_and_store(float (&acc)[RB][4], float *red, int W, int wave,
                                                  int lane, int b, int64_t n0, int64_t N,
                                                  const float (&tsc)[4], void *y, int y_dtype) {
-  const int col = lane & 15, qd = lane >> 4;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[rb][i] *= tsc[i];
-  if (W > 1) {
-    if (wave > 0) {
+  if (W == 1) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int i = 0; i < NT; ++i) red[(((wave - 1) * RB + rb) * NT + i) * 64 + lane] = acc[rb][i];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-    for (int w = 1; w < W; ++w)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < NT; ++i) acc[rb][i] += red[(((w - 1) * RB + rb) * NT + i) * 64 + lane];
+      for (int i = 0; i < NT; ++i) store_out<LP>(acc[rb][i], rb, i, lane, b, n0, N, y, y_dtype);
+    return;
   }
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int t = LP ? 2 * qd + i : 4 * i + qd;  // token of accumulator i
-    if (t >= b) continue;
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int64_t n = n0 + 16 * rb + col;
-      if (n >= N) continue;
-      const float v = acc[rb][i];
-      if (y_dtype == TL_F32)
-        reinterpret_cast<float *>(y)[int64_t(t) * N + n] = v;
-      else
-        reinterpret_cast<uint16_t *>(y)[int64_t(t) * N + n] = float_to_bf16_bits(v);
-    }
+    for (int i = 0; i < NT; ++i) red[((wave * RB + rb) * NT + i) * 64 + lane] = acc[rb][i];
+  __syncthreads();
+  for (int c = wave; c < RB * NT; c += W) {
+    const int rb = c / NT, i = c - rb * NT;
+    float v = red[(rb * NT + i) * 64 + lane];
+    for (int w = 1; w < W; ++w) v += red[((w * RB + rb) * NT + i) * 64 + lane];
+    store_out<LP>(v, rb, i, lane, b, n0, N, y, y_dtype);
   }
 }
+
+// --------------------------------------------------------------------------
+// phase timestamps of gemv_stream (instrumented builds only: TL_PHASE_STAMPS=1)
+// --------------------------------------------------------------------------
+// Each wave keeps the constant-rate clock (100 MHz) at its phase boundaries in
+// registers -- entry, every load issued, direct loads waited for, barrier
+// passed, first pair computed, last pair computed -- and stores them, with its
+// hardware id, before the cross-wave reduction; wave 0 adds the time its
+// outputs were stored.  Record w = (blockIdx.y * gridDim.x + blockIdx.x) * 16 +
+// wave, eight 64-bit words.  No store happens before the reduction, so the
+// kernel's own memory waits are unchanged.  Off in the product build, where the
+// calls are empty.
+#ifndef TL_PHASE_STAMPS
+#define TL_PHASE_STAMPS 0
+#endif
+#if TL_PHASE_STAMPS
+__device__ unsigned long long *g_phase_stamps;
+struct PhaseStamps {
+  unsigned long long t[6];
+  __device__ __forceinline__ void mark(int k) { t[k] = wall_clock64(); }
+  __device__ __forceinline__ unsigned long long *record() const {
+    unsigned long long *base = g_phase_stamps;
+    return base ? base + ((int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * 16 + (threadIdx.x >> 6)) * 8 : nullptr;
+  }
+  __device__ __forceinline__ void flush() const {
+    unsigned long long *r = record();
+    if (!r || (threadIdx.x & 63) != 0) return;
+    unsigned hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+#pragma unroll
+    for (int k = 0; k < 6; ++k) r[k] = t[k];
+    r[7] = (unsigned long long)hw | ((unsigned long long)xcc << 32);
+  }
+  __device__ __forceinline__ void done() const {
+    unsigned long long *r = record();
+    if (r && (threadIdx.x & 63) == 0) r[6] = wall_clock64();
+  }
+};
+#else
+struct PhaseStamps {
+  __device__ __forceinline__ void mark(int) {}
+  __device__ __forceinline__ void flush() const {}
+  __device__ __forceinline__ void done() const {}
+};
+#endif
 
 // --------------------------------------------------------------------------
 // gemv_stream: every load of the wave issued at once, pairs consumed as they land
@@ -396,6 +446,8 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
   constexpr int NA = LP ? 4 : 8;  // A fragment loads per pair when not ALDS
   extern __shared__ __attribute__((aligned(16))) char smem[];
   static_assert(PMAX <= 5, "a wave's pairs span at most two 1024-blocks");
+  PhaseStamps ps;
+  ps.mark(0);
   select_chunk(limbs, sigma, y, b, K, N, y_dtype);
   const int64_t region = LP ? limb_region_bytes(b, K) : 32 * K;  // this chunk's limbs
   int8_t *lx = reinterpret_cast<int8_t *>(smem);
@@ -476,14 +528,17 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
       wv[pi][rb] = load_tile(packed, min(int64_t(blockIdx.x) * RB + rb, NB - 1), GP, p, lane);
   }
   asm volatile("" ::: "memory");
+  ps.mark(1);
   // 3. wait for the direct loads only; the register loads may stay in
   //    flight.  With limbs in LDS nothing may be scheduled above this point: work
   //    on a tile moved up here would make the wait cover every load (the counter
   //    is in order).  With limbs in registers the compiler's own interleaving of
   //    the first pairs' matrix instructions with the loads is the faster one.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm<PMAX * (RB + (ALDS ? 0 : NA))>());
+  ps.mark(2);
   __builtin_amdgcn_s_barrier();
   if constexpr (ALDS) __builtin_amdgcn_sched_barrier(0);
+  ps.mark(3);
 
   // 4. pairs in arrival order.  LDS is read through lds_read* so that the
   //    compiler, which cannot tell these reads from the destinations of the
@@ -551,7 +606,9 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
       }
     }
     pair_mfma<RB, NT, LP>(ah, al, wv[pi], sv, acc);
+    if (pi == 0) ps.mark(4);
   }
+  ps.mark(5);
   // each block's sums times its limb scales (and the 1/64 of the unpacked codes);
   // every LDS read of the loop has been waited for
   float ua[4], ub[ALDS ? 4 : 1];
@@ -571,8 +628,10 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
 #pragma unroll
       for (int i = 0; i < NT; ++i) acc[rb][i] *= ua[i];
   }
+  ps.flush();
   __syncthreads();  // every wave is done with LDS before `red` is written
   reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
+  ps.done();
 }
 
 // --------------------------------------------------------------------------
@@ -779,7 +838,7 @@ __global__ __launch_bounds__(64 * GemvWaveCap<RB>::value) void gemv_ring_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   select_chunk(limbs, sigma, y, b, K, N, y_dtype);
   // scale block of the workgroup's rows, the chunk's limb scales [b][nbk], then
-  // (W - 1) * RB * NT * 64 floats
+  // W * RB * NT * 64 floats
   char *ls = smem;
   float *lsig = reinterpret_cast<float *>(smem + scale_lds_bytes(16 * RB, int(K / kGroup)));
   float *red = reinterpret_cast<float *>(reinterpret_cast<char *>(lsig) + ring_sig_bytes(K));
@@ -957,7 +1016,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
                        : rows48 >= 3 * kCUs / 4 ? 3 : 2;
       const size_t lds = lds_limbs + scale_lds_bytes(16 * pref, int(G)) + kSigLds;
       if (shape(true, pref, pmax0) &&
-          lds + size_t(p.waves > 1 ? p.waves - 1 : 1) * pref * nt * 256 <= size_t(kLdsPerCU))
+          lds + size_t(p.waves) * pref * nt * 256 <= size_t(kLdsPerCU))
         return pref;
     }
     int best = 0;
@@ -965,7 +1024,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     for (int rb = 1; rb <= 4; ++rb) {
       if (!shape(alds, rb, pmax0) || (!alds && straddles(GP, p.waves))) continue;
       const size_t lds = lds_limbs + scale_lds_bytes(16 * rb, int(G)) + kSigLds +
-                         size_t(p.waves > 1 ? p.waves - 1 : 1) * rb * nt * 256;
+                         size_t(p.waves) * rb * nt * 256;
       if (lds > size_t(kLdsPerCU)) continue;
       int64_t per_cu = stream_resident(alds, rb, b, p.pmax, p.waves, lds);
       if (per_cu <= 0) {  // no answer from the runtime: bound by LDS and the register budget
@@ -1011,7 +1070,7 @@ GemvPlan plan_gemv(int64_t b, int64_t K, int64_t N) {
     p.lds_limb_bytes = 0;
   }
   p.lds_bytes = size_t(p.lds_limb_bytes) + scale_lds_bytes(16 * p.rb, int(G)) + (p.kind == 2 ? ring_sig_bytes(K) : kSigLds) +
-                size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * nt * 64 * sizeof(float);
+                size_t(p.waves) * p.rb * nt * 64 * sizeof(float);
   p.name = variant_name(p.kind, p.rb, p.waves, p.pmax);
   p.chunks = int(chunks);
   p.ok = p.lds_bytes <= size_t(kLdsPerCU) && p.waves >= 1 && 64 * p.waves <= 1024 &&
@@ -1120,7 +1179,7 @@ Q8Plan plan_q8(int64_t b, int64_t K, int64_t N) {
     }
   }
   p.lds = size_t(p.lds_a) + scale_lds_bytes(16 * p.rb, int(G)) +
-          size_t(p.waves > 1 ? p.waves - 1 : 1) * p.rb * p.nt * 64 * sizeof(float);
+          size_t(p.waves) * p.rb * p.nt * 64 * sizeof(float);
   p.ok = p.lds <= size_t(kLdsPerCU);
   static const char *names[2][2] = {{"gemv_q8_reg_rb1", "gemv_q8_reg_rb2"}, {"gemv_q8_lds_rb1", "gemv_q8_lds_rb2"}};
   p.name = names[p.alds ? 1 : 0][p.rb - 1];
@@ -1353,6 +1412,13 @@ void launch_rot_t(int nblk, const uint16_t *x, const int8_t *signs, int64_t K, i
 }
 
 }  // namespace
+
+#if TL_PHASE_STAMPS
+// where gemv_stream writes its phase timestamps (NULL: nowhere); instrumented builds only
+extern "C" int tl_phase_stamps_set(void *device_buffer) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stamps), &device_buffer, sizeof(device_buffer)) == hipSuccess ? 0 : 1;
+}
+#endif
 
 bool gemv_supported(int64_t b, int64_t K, int64_t N) {
   return b <= 0 || N <= 0 || plan_gemv(b, K, N).ok;
