@@ -83,6 +83,9 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="write the HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                         "counter CSVs of this bench (--steps S --warmup W) and of --calib-copy, then exit")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "STATS_CSV"),
+                   help="print the per-launch device time of the GEMV and GEMM launches from a rocprofv3 "
+                        "--kernel-trace --stats run of this bench, and the library's kernel statistics, then exit")
     return p.parse_args()
 
 
@@ -149,6 +152,38 @@ def summarize_counters(paths):
         label = f"decode GEMV qkv b={key}" if fam == "gemv" else f"prefill GEMM {key}"
         vals = " | ".join(f"{float(np.median(e[c])):.4g}" if c in e else "-" for c in counters)
         print(f"| {label} | `{e['kernel']}` | {len(e[counters[0]])} | {vals} |")
+
+
+def summarize_trace(trace_csv, stats_csv):
+    """Per-launch device time (kernel trace) of the bench's GEMV and GEMM launches, as
+    markdown: count, mean, median, p10, p90 in µs; then the library's rows of the
+    --stats table."""
+    import csv
+    with open(trace_csv, newline="") as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    durs = [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in rows]
+    groups = {}
+    for fam, key, kname, v in _attribute(durs):
+        groups.setdefault((fam, key), (kname, []))[1].append(v)
+    print("| launch | kernel | launches | mean µs | median µs | p10 µs | p90 µs |")
+    print("|---|---|---|---|---|---|---|")
+    labels = {"gate_up": "gate_up 5120→34816", "down": "down 17408→5120"}
+    for (fam, key), (kname, v) in groups.items():
+        d = np.sort(np.asarray(v))
+        name = (f"decode GEMV qkv 5120→10240 b={key}" if fam == "gemv" else f"prefill GEMM M={PREFILL_M} {labels[key]}")
+        print(f"| {name} | `{kname}` | {len(d)} | {d.mean():.2f} | {np.median(d):.2f} | "
+              f"{np.percentile(d, 10):.2f} | {np.percentile(d, 90):.2f} |")
+    print()
+    with open(stats_csv, newline="") as f:
+        stats = list(csv.DictReader(f))
+    print("| kernel | calls | avg µs | min µs | max µs | % |")
+    print("|---|---|---|---|---|---|")
+    for r in stats:
+        name = _short_name(r["Name"] + "(")
+        if not any(k in name for k in ("gemv_", "gemm_", "spin_kernel", "read_probe")):
+            continue
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+              f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
 
 
 def summarize_pmc(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
@@ -240,6 +275,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the "
