@@ -23,8 +23,12 @@
 //    waits (the compiler would otherwise wait for every load before them);
 //  * packed weight words arrive in a two-deep register ring, loaded straight
 //    from the 1 KB packed tiles (two 16-byte loads per column per pair);
-//  * the LDS reads and the weight expansion of k-step s+1 are issued between the
-//    MFMAs of k-step s, and there is one barrier per pair.
+//  * the LDS reads of k-step s+1 are issued between the MFMAs of k-step s, and
+//    the codes are expanded column by column: while the MFMAs of weight column j
+//    run, column j+1 (or column 0 of the next k-step) is expanded into registers
+//    whose readers have all been issued; there is one barrier per pair;
+//  * the tile's row scales wait in LDS for the epilogue, so that no register is
+//    held for them through the K loop.
 // The expansion code -> code*q is one v_perm_b32 per 4 weights: the selector
 // bytes are the 2-bit fields ((w >> 2r) & 0x03030303) and the table holds
 // {0, q, -, -q}.
@@ -162,6 +166,13 @@ __device__ __forceinline__ void fetch_b(v4i (&bf)[J], const BStage<J> &b, int s)
 #pragma unroll
   for (int j = 0; j < J; ++j)
     bf[j] = expand_word(b.w[j][ss >> 1][2 * gi + (ss & 1)], perm_table(b.q[j][gi]) & b.keep[gi]);
+}
+
+// column j only: the fragment of k-step s for the lane's j-th weight column
+template <int J>
+__device__ __forceinline__ v4i fetch_col(const BStage<J> &b, int s, int j) {
+  const int gi = s >> 2, ss = s & 3;
+  return expand_word(b.w[j][ss >> 1][2 * gi + (ss & 1)], perm_table(b.q[j][gi]) & b.keep[gi]);
 }
 
 template <int MT, int J>
@@ -404,17 +415,41 @@ __device__ __forceinline__ void pair_body2(int p, int k0, int plast, const Frame
       wait_a2<MT, 0>(af[s & 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step(af[s & 1], bf[s & 1], acc);
-    if (s < 7)
-      fetch_b(bf[(s + 1) & 1], ring[S], s + 1);
-    else
-      fetch_b(bf[0], ring[S ^ 1], 0);
+    if constexpr (J >= 2) {
+      // column by column: the MFMAs of column j read fragment j of this k-step
+      // while the next fragment (column j + 1, or column 0 of the next k-step)
+      // is expanded into the registers whose readers have all been issued
 #pragma unroll
-    for (int i = 0; i < MT * J; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+      for (int j = 0; j < J; ++j) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s & 1][mt], bf[0][j], acc[mt][j], 0, 0, 0);
+        if (j + 1 < J)
+          bf[0][j + 1] = fetch_col(ring[S], s, j + 1);
+        else if (s < 7)
+          bf[0][0] = fetch_col(ring[S], s + 1, 0);
+        else
+          bf[0][0] = fetch_col(ring[S ^ 1], 0, 0);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // up to three VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      mfma_step(af[s & 1], bf[s & 1], acc);
+      if (s < 7)
+        fetch_b(bf[(s + 1) & 1], ring[S], s + 1);
+      else
+        fetch_b(bf[0], ring[S ^ 1], 0);
+#pragma unroll
+      for (int i = 0; i < MT * J; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to four VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     if (s == 7) load_b(ring[S], f, min(max(p + 2, k0), plast), p + 2 >= k0);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -454,15 +489,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
   }
   // token scales of the tile's rows (LDS, read in the epilogue) and this lane's row scales
   if (tid < T::BM) s_tok[tid] = a.tok_scale[m0 + tid < M ? m0 + tid : M - 1];
-  float rsv[J];
+  // row scales of the tile's columns: LDS until the epilogue (no registers held
+  // through the K loop)
+  float *s_rsv = s_tok + kBM;
+  if (tid < T::BN) s_rsv[tid] = a.row_scale[n0 + tid < N ? n0 + tid : N - 1];
   // weight columns of this lane: one per 32-wide N tile, read from the packed tiles
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int c = 32 * J * wave + 32 * j + l32;     // column inside the tile
     f.boff[j] = (c >> 4) * GP * 1024 + 16 * (32 * h + (c & 15));
     f.qoff[j] = c * G;
-    const int64_t n = n0 + c;
-    rsv[j] = a.row_scale[n < N ? n : N - 1];
   }
 
   v16i acc[MT][J];
@@ -489,7 +525,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
   const uint32_t rowaddr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t *)sA + 256 * l32;
   const int xsw = l32 & 15;
   v4i af[2][MT], bf[2][J];
-  fetch_b(bf[0], ring[0], 0);
+  if constexpr (J >= 2)
+    bf[0][0] = fetch_col(ring[0], 0, 0);  // the other columns are expanded inside the loop
+  else
+    fetch_b(bf[0], ring[0], 0);
   for (int p = p0; p < k1; p += 2) {
     pair_body2<0, MT, J>(p, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
     pair_body2<1, MT, J>(p + 1, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
@@ -545,6 +584,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
       __hip_atomic_store(&a.counters[tile - sc.full], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  float rsv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) rsv[j] = s_rsv[32 * J * wave + 32 * j + l32];
   const bool whole = m0 + T::BM <= M && n0 + T::BN <= N;
   if (whole && !a.acc_out && N % 8 == 0) {  // rows of y start on 16-byte boundaries
     if (a.y_dtype == TL_F32) epilogue_lds<true, MT, J, kStageLds>(acc, s_tok, rsv, m0, n0, N, wave, l32, h, tid, a.y, sA);
@@ -583,7 +625,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemm_i8_kernel(
     int32_t *__restrict__ acc_out, int32_t *__restrict__ part, int32_t *__restrict__ counters,
     Schedule sc) {
   __shared__ __attribute__((aligned(16))) int8_t sA[kStageLds];
-  __shared__ __attribute__((aligned(16))) float s_tok[kBM];
+  __shared__ __attribute__((aligned(16))) float s_tok[kBM + kBN];  // token scales, then row scales
   __shared__ int s_last;
   const GemmArgs a{xq, tok_scale, M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters};
   const int GP = int((K / kGroup + 1) / 2);
