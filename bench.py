@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
 
 DECODE_BS = (1, 4, 8, 16)
 PREFILL_M = 512
+MFMA_PROBE_GRID = 512        # workgroups of tl_mfma_probe (four waves each)
 DEC_LAYERS = 8     # qkv-shaped layers per decode pass (distinct weight copies)
 PRE_LAYERS = 2     # layers of each MLP type per prefill pass
 
@@ -180,7 +181,7 @@ def summarize_trace(trace_csv, stats_csv):
     print("|---|---|---|---|---|---|")
     for r in stats:
         name = _short_name(r["Name"] + "(")
-        if not any(k in name for k in ("gemv_", "gemm_", "spin_kernel", "read_probe")):
+        if not any(k in name for k in ("gemv_", "gemm_", "spin_kernel", "read_probe", "mfma_probe")):
             continue
         print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
               f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
@@ -544,6 +545,18 @@ def main():
     nb = qkv[0][0].numel() * 4
     floor["read_codes"] = {"bytes": int(nb), "us": round(t_read * 1e6, 2), "GBps": round(nb / t_read / 1e9, 1),
                            "kernel": "read_probe"}
+    # the matrix-core floor: one launch of back-to-back int8 32x32x32 MFMAs on every
+    # SIMD (two waves each, eight independent chains per wave), no memory traffic,
+    # with constant operands and with random ones; the GEMM's own rate compares
+    # with the random figure, since its operands are random int8 too
+    mf_iters = 2000
+    mf_ops = MFMA_PROBE_GRID * 4 * mf_iters * 8 * 2 * 32 * 32 * 32
+    mfma_ceiling = {"ops_per_launch": int(mf_ops)}
+    for name, rnd in (("constant", False), ("random", True)):
+        t_m = run_time(lambda: tl.mfma_probe(rnd, mf_iters, sink_t), n=5) * 1e-3
+        mfma_ceiling[name] = {"us": round(t_m * 1e6, 1), "TOPs": round(mf_ops / t_m / 1e12, 1),
+                              "frac_of_peak": round(mf_ops / t_m / 1e12 / INT8_PEAK_TOPS, 4),
+                              "kernel": "mfma_probe_" + name}
     # the whole decode layer from the raw bf16 input (rotation, limbs, GEMV): one
     # launch for b <= 2 at this shape, else the fused rotation + limb prep and the GEMV
     layer = {}
@@ -641,6 +654,7 @@ def main():
                                                    (float(np.mean(v)) * 1e-3) / 1e9, 1)
                                           for k, v in quant_ms.items()}},
         "launch_floor": floor,
+        "mfma_ceiling": mfma_ceiling,
         "input_kernels_us": {
             "decode_rotate_prep": {str(b): round(float(np.mean(prep_ms[b])) * 1e3, 2) for b in DECODE_BS},
             "prefill_rotate_quant_m512": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in quant_ms.items()},

@@ -351,6 +351,20 @@ int tl_linear_apply(const uint16_t *x, int64_t T, int64_t K, int64_t N, const in
 int tl_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 /*
+ * tl_mfma_probe -- measurement helper, not a step of the layer: one launch of 512
+ * workgroups of 256 threads (two per compute unit, as the prefill GEMM runs) in
+ * which every wavefront issues iters x 8 v_mfma_i32_32x32x32_i8 on eight
+ * independent accumulators (65536 int8 operations each) and nothing else, with
+ * constant operands (random_operands = 0: every byte 1) or random-looking ones
+ * (a hash of the lane and workgroup).  Its duration gives the int8 matrix-core
+ * rate the chip sustains with each kind of data, beside which the GEMM's can be
+ * put: 512 * 4 * iters * 8 * 65536 operations.  sink is a device pointer,
+ * 16-byte aligned, of which at most one word is written.
+ * Errors: TL_ERR_SHAPE for iters <= 0, TL_ERR_NULLPTR, TL_ERR_ALIGN.
+ */
+int tl_mfma_probe(int random_operands, int iters, uint32_t *sink, void *stream);
+
+/*
  * tl_linear_apply_noalloc -- tl_linear_apply without a workspace argument and
  * without any allocation, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid it.

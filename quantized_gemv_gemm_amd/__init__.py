@@ -59,6 +59,7 @@ _SIGS = {
                                        ctypes.c_int, _c_p, _c_sz, _c_p]),
     "tl_noalloc_scratch_bytes": (_c_sz, []),
     "tl_read_probe": (ctypes.c_int, [_c_p, _c_sz, _c_p, _c_p]),
+    "tl_mfma_probe": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _c_p, _c_p]),
     "tl_linear_apply_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p,
                                                _c_p, ctypes.c_int, _c_p]),
 }
@@ -469,6 +470,15 @@ def read_probe(src, sink):
         raise ValueError("read_probe needs contiguous device tensors")
     nbytes = src.numel() * src.element_size() // 16 * 16
     _check("tl_read_probe", lib().tl_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(src.device)))
+
+
+def mfma_probe(random_operands, iters, sink):
+    """Measurement helper: one launch that only issues int8 matrix instructions
+    (see tl_mfma_probe); ``sink`` is a 4-byte (or larger) device tensor."""
+    if not sink.is_cuda:
+        raise ValueError("mfma_probe needs a device tensor")
+    _check("tl_mfma_probe", lib().tl_mfma_probe(1 if random_operands else 0, int(iters), _ptr(sink),
+                                                _stream(sink.device)))
 
 
 def noalloc_scratch_bytes() -> int:

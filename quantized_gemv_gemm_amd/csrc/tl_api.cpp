@@ -308,6 +308,13 @@ int tl_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
   return from_hip(tl::launch_read_probe(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int tl_mfma_probe(int random_operands, int iters, uint32_t *sink, void *stream) {
+  if (iters <= 0) return TL_ERR_SHAPE;
+  if (!sink) return TL_ERR_NULLPTR;
+  if (!aligned16(sink)) return TL_ERR_ALIGN;
+  return from_hip(tl::launch_mfma_probe(random_operands ? 1 : 0, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
 size_t tl_gemm_workspace_size(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || N < 0 || K <= 0 || K % tl::kGroup) return 0;
   return tl::gemm_workspace_bytes(M, K, N);

@@ -92,6 +92,7 @@ hipError_t launch_hadamard_join(const double *u_lo, const double *u_hi, int64_t 
 
 // measurement helper: a launch that only reads `bytes` (k_probe.hip)
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+hipError_t launch_mfma_probe(int random, int iters, uint32_t *sink, hipStream_t stream);
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int64_t K, int64_t N,

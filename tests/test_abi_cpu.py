@@ -241,3 +241,6 @@ def test_read_probe_rejections():
     assert L.tl_read_probe(None, 1024, FAKE2, None) == 1
     assert L.tl_read_probe(ODD, 1024, FAKE2, None) == 3
     assert L.tl_read_probe(FAKE, 1024, FAKE, None) == 8      # sink inside the source
+    assert L.tl_mfma_probe(1, 0, FAKE2, None) == 2            # no iterations
+    assert L.tl_mfma_probe(0, 10, None, None) == 1
+    assert L.tl_mfma_probe(1, 10, ODD, None) == 3
