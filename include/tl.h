@@ -356,7 +356,8 @@ int tl_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
  * which every wavefront issues iters x 8 v_mfma_i32_32x32x32_i8 on eight
  * independent accumulators (65536 int8 operations each) and nothing else, with
  * constant operands (random_operands = 0: every byte 1) or random-looking ones
- * (a hash of the lane and workgroup).  Its duration gives the int8 matrix-core
+ * (two sets hashed from the lane and workgroup, alternating from one
+ * instruction to the next).  Its duration gives the int8 matrix-core
  * rate the chip sustains with each kind of data, beside which the GEMM's can be
  * put: 512 * 4 * iters * 8 * 65536 operations.  sink is a device pointer,
  * 16-byte aligned, of which at most one word is written.
