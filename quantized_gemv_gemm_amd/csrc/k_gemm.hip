@@ -396,12 +396,15 @@ __device__ __forceinline__ void dma_a2(const Frame<J> &f, int8_t *buf, int p, in
 #endif
 }
 
-template <int S, int MT, int J>
+template <int S, int MT, int J, bool kPrio>
 __device__ __forceinline__ void pair_body2(int p, int k0, int plast, const Frame<J> &f, int8_t *sA,
                                            uint32_t rowaddr, int xsw, int h, int wave, int dvoff, int64_t K,
                                            BStage<J> (&ring)[2], v4i (&af)[2][MT], v4i (&bf)[2][J],
                                            v16i (&acc)[MT][J]) {
   constexpr int AB = Tile<MT, J>::BM * 256;
+  // the pair boundary (stage loads, first operand reads, the barrier) runs at the
+  // normal issue priority, the middle k-steps at the raised one (kPrio)
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
   // the next pair's stage into the other buffer (every wave left it at the last barrier)
   dma_a2<MT, J>(f, sA + (S ^ 1) * AB, min(max(p + 1, k0), plast), wave, dvoff, K);
   const uint32_t cur = rowaddr + S * AB;
@@ -450,7 +453,11 @@ __device__ __forceinline__ void pair_body2(int p, int k0, int plast, const Frame
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (s == 7) load_b(ring[S], f, min(max(p + 2, k0), plast), p + 2 >= k0);
+    if (kPrio && s == 0) __builtin_amdgcn_s_setprio(1);
+    if (s == 7) {
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
+      load_b(ring[S], f, min(max(p + 2, k0), plast), p + 2 >= k0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   // this wave's stage loads are done (the weight loads just issued may stay in flight)
@@ -459,9 +466,10 @@ __device__ __forceinline__ void pair_body2(int p, int k0, int plast, const Frame
 }
 
 // One workgroup tile of 32 MT x 128 J at (m0, n0) over the pairs [k0, k1).  A
-// piece of a K-split tile (piece >= 0, big tiles only) publishes its partial
-// tile and only the last piece to arrive runs the epilogue.
-template <int MT, int J>
+// piece of a K-split tile (piece >= 0) publishes its partial tile and only the
+// last piece to arrive runs the epilogue.  kPrio: the middle k-steps of each pair
+// run at a raised issue priority (see gemm_i8_kernel).
+template <int MT, int J, bool kPrio>
 __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, int8_t *sA, float *s_tok,
                                          int *s_last, int64_t m0, int64_t n0, int k0, int k1, int tile,
                                          int piece, int slot) {
@@ -530,10 +538,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &a, const Schedule &sc, 
   else
     fetch_b(bf[0], ring[0], 0);
   for (int p = p0; p < k1; p += 2) {
-    pair_body2<0, MT, J>(p, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
-    pair_body2<1, MT, J>(p + 1, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
+    pair_body2<0, MT, J, kPrio>(p, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
+    pair_body2<1, MT, J, kPrio>(p + 1, k0, plast, f, sA, rowaddr, xsw, h, wave, dvoff, K, ring, af, bf, acc);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the loop
+  if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
 
   if (piece >= 0) {
     // Split tile: publish this piece, and only the last piece to arrive goes on.
@@ -618,6 +627,15 @@ __device__ __forceinline__ int xcd_item(int e, int total) {
   return (total / kXcds) * (e % kXcds) + e / kXcds;
 }
 
+// kPrio (the host sets it when the whole grid is resident at once, two
+// workgroups per CU): a wave raises its issue priority for the middle k-steps of
+// each pair and drops it for the pair boundary, so a workgroup at its boundary
+// yields the SIMDs to the other workgroup of its CU, and the two progress evenly
+// instead of the older one finishing first.  When more workgroups follow, the
+// whole tiles of the first rounds keep the uneven progress (the first to finish
+// hands its slot on early); the left-over work that comes last in the grid (K
+// pieces, sub-tiles) always raises it.
+template <bool kPrio>
 __global__ __launch_bounds__(kThreads, kWgPerCu) void gemm_i8_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ tok_scale, int64_t M, int64_t K,
     int64_t N, const uint32_t *__restrict__ packed, const int8_t *__restrict__ q,
@@ -651,7 +669,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemm_i8_kernel(
     }
     const int64_t m0 = int64_t(tile % sc.mb) * Mid::BM;
     const int64_t n0 = int64_t(tile / sc.mb) * Mid::BN;
-    run_tile<Mid::BM / 32, Mid::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);
+    if (kPrio || g >= sc.full)
+      run_tile<Mid::BM / 32, Mid::BN / 128, true>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);
+    else
+      run_tile<Mid::BM / 32, Mid::BN / 128, false>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, e);
     return;
   }
   if (g >= sc.full && sc.narrow) {
@@ -662,7 +683,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemm_i8_kernel(
     const int64_t m0 = int64_t(tile % sc.mb) * kBM + Narrow::BM * (u % kRowCuts);
     const int64_t n0 = int64_t(tile / sc.mb) * kBN + Narrow::BN * (u / kRowCuts);
     if (m0 >= M || n0 >= N) return;  // the whole sub-tile lies past the output
-    run_tile<Narrow::BM / 32, Narrow::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
+    run_tile<Narrow::BM / 32, Narrow::BN / 128, true>(a, sc, sA, s_tok, &s_last, m0, n0, 0, GP, tile, -1, 0);
     return;
   }
   int tile, piece = -1, slot = 0, k0 = 0, k1 = GP;
@@ -680,7 +701,10 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void gemm_i8_kernel(
   }
   const int64_t m0 = int64_t(tile % sc.mb) * kBM;
   const int64_t n0 = int64_t(tile / sc.mb) * kBN;
-  run_tile<Big::BM / 32, Big::BN / 128>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
+  if (kPrio || g >= sc.full)
+    run_tile<Big::BM / 32, Big::BN / 128, true>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
+  else
+    run_tile<Big::BM / 32, Big::BN / 128, false>(a, sc, sA, s_tok, &s_last, m0, n0, k0, k1, tile, piece, slot);
 }
 
 // Workspace layout, the same for every shape so that one workspace serves calls
@@ -709,8 +733,12 @@ hipError_t launch_gemm(const int8_t *xq, const float *tok_scale, int64_t M, int6
     part = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + kCounterBytes);
   }
   (void)hipGetLastError();  // drop errors left by earlier, unrelated runtime calls
-  hipLaunchKernelGGL(gemm_i8_kernel, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale, M, K,
-                     N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
+  if (s.grid() <= 2 * kSlots)
+    hipLaunchKernelGGL(gemm_i8_kernel<true>, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
+                       M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
+  else
+    hipLaunchKernelGGL(gemm_i8_kernel<false>, dim3(unsigned(s.grid())), dim3(kThreads), 0, stream, xq, tok_scale,
+                       M, K, N, packed, q, row_scale, y, y_dtype, acc_out, part, counters, s);
   static const char *names[3] = {"gemm_i8_mfma32_128x256_lds2", "gemm_i8_mfma32_128x256_lds2_splitk",
                                   "gemm_i8_mfma32_128x256_lds2_narrowtail"};
   if (s.mid)

@@ -53,6 +53,8 @@ def test_other_kernels_use_no_scratch(resources):
 def test_gemm_holds_two_workgroups_per_cu(resources):
     """The GEMM schedule assumes two 256-thread workgroups per compute unit: its
     registers must leave two waves per SIMD and its LDS two workgroups."""
-    (fig,) = [v for k, v in resources.items() if "gemm_i8_kernel" in k]
-    assert fig["occupancy"] >= 2
-    assert 2 * fig["lds"] <= 160 * 1024
+    figs = [v for k, v in resources.items() if "gemm_i8_kernel" in k]
+    assert len(figs) == 2          # the launches with and without the raised issue priority
+    for fig in figs:
+        assert fig["occupancy"] >= 2
+        assert 2 * fig["lds"] <= 160 * 1024
