@@ -270,8 +270,9 @@ __device__ __forceinline__ void epilogue_lds(const v16i (&acc)[MT][J], const flo
 #pragma unroll
     for (int k = tid; k < ROWS * CPR; k += kThreads) {
       const int r = k / CPR, cc = k - r * CPR;
-      *reinterpret_cast<v4u *>(ybase + (int64_t(r) * N) * ES + 16 * cc) =
-          *reinterpret_cast<const v4u *>(stage + r * PITCH + 16 * cc);
+      // non-temporal: the output is not read again by this launch
+      __builtin_nontemporal_store(*reinterpret_cast<const v4u *>(stage + r * PITCH + 16 * cc),
+                                  reinterpret_cast<v4u *>(ybase + (int64_t(r) * N) * ES + 16 * cc));
     }
     if (pass + 1 < BM / ROWS) __syncthreads();  // the next pass overwrites the staging rows
   }
