@@ -50,6 +50,12 @@
 // problem takes 128 x 128 tiles (each wave 128 x 32) on the two-per-CU pipeline
 // instead: whole rounds of 512, the rest split along K into at most 6 pieces.
 // No workgroup ever waits for another.
+//
+// Issue priority: when the whole grid is resident at once, the waves raise
+// their priority (s_setprio) for the middle k-steps of each pair, so that the
+// two workgroups of a compute unit progress evenly; the left-over work at the
+// end of a longer grid does the same (see gemm_i8_kernel).  Whole tiles store
+// their output non-temporally.
 #include <algorithm>
 
 #include "tl_device.h"
