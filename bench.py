@@ -34,6 +34,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import synth  # noqa: E402  (seeded input recipes; no arithmetic of the method)
+
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, TOP/s
 MALL_BYTES = 256 * 2 ** 20
@@ -51,6 +53,8 @@ PREFILL_M = 512
 MFMA_PROBE_GRID = 512        # workgroups of tl_mfma_probe (four waves each)
 DEC_LAYERS = 8     # qkv-shaped layers per decode pass (distinct weight copies)
 PRE_LAYERS = 2     # layers of each MLP type per prefill pass
+# random-stream numbers of the synthetic workloads
+S_DEC, S_MLP, S_PRE = (synth.WORKLOADS[w]["stream"] for w in ("decode_qkv", "decode_mlp", "prefill_mlp"))
 
 
 def gemv_bytes(b, K, N):
@@ -281,8 +285,8 @@ def main():
         summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build measures the "
-              "single-GPU kernels; multi-GPU sharding is design-only.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures the "
+              "single-GPU kernels; sharding across GPUs is described, not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -320,8 +324,8 @@ def main():
         return
 
     # ---------------- weights (packed once, cloned into rotating copies) ----------------
-    def make_layer(config, li, K, N):
-        L = synth.LayerInputs(0, config, li, K, N)
+    def make_layer(stream, li, K, N):
+        L = synth.LayerInputs(0, stream, li, K, N)
         codes = L.codes_torch(dev)
         scales = torch.from_numpy(L.scales()).to(dev)
         packed, q, rs = tl.pack_weights(codes, scales)
@@ -332,10 +336,10 @@ def main():
                                               for _ in range(R - 1)]
         return copies
 
-    log("packing qkv (config 1) and prefill layers (config 3)")
-    qkv = make_layer(1, 0, 5120, 10240)
-    gate_up = make_layer(3, 0, 5120, 34816)
-    down = make_layer(3, 1, 17408, 5120)
+    log("packing the decode qkv layer and the prefill MLP layers")
+    qkv = make_layer(S_DEC, 0, 5120, 10240)
+    gate_up = make_layer(S_PRE, 0, 5120, 34816)
+    down = make_layer(S_PRE, 1, 17408, 5120)
     torch.cuda.synchronize()
     log(f"rotating copies: qkv {len(qkv)}, gate_up {len(gate_up)}, down {len(down)}")
 
@@ -348,7 +352,7 @@ def main():
         return
 
     Kq, Nq = 5120, 10240
-    x_dec = {b: bf16(synth.activations(0, 1, 0, b, Kq)) for b in DECODE_BS}
+    x_dec = {b: bf16(synth.activations(0, S_DEC, 0, b, Kq)) for b in DECODE_BS}
     ws_dec = {b: torch.empty((tl.gemv_workspace_size(b, Kq, Nq),), dtype=torch.uint8, device=dev)
               for b in DECODE_BS}
     y_dec = {b: torch.empty((b, Nq), dtype=torch.bfloat16, device=dev) for b in DECODE_BS}
@@ -356,7 +360,7 @@ def main():
     pre = {}
     for name, copies, li, K, N in (("gate_up", gate_up, 0, 5120, 34816), ("down", down, 1, 17408, 5120)):
         pre[name] = dict(copies=copies, K=K, N=N,
-                         x=bf16(synth.activations(0, 3, li, PREFILL_M, K)),
+                         x=bf16(synth.activations(0, S_PRE, li, PREFILL_M, K)),
                          xq=torch.empty((PREFILL_M, K), dtype=torch.int8, device=dev),
                          sx=torch.empty((PREFILL_M,), dtype=torch.float32, device=dev),
                          y=torch.empty((PREFILL_M, N), dtype=torch.bfloat16, device=dev))
@@ -483,7 +487,7 @@ def main():
     for b in (1, 16):
         rows = []
         for name, copies, K, N in floor_shapes:
-            xr = tl.hadamard_blk(bf16(synth.activations(0, 2, 7, b, K)))
+            xr = tl.hadamard_blk(bf16(synth.activations(0, S_MLP, 7, b, K)))
             ws = torch.empty((tl.gemv_workspace_size(b, K, N),), dtype=torch.uint8, device=dev)
             yb = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
             tl.gemv_prepare(xr, ws)
@@ -698,7 +702,7 @@ def library_reference(tl, torch, dev, n=20):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e3
     for (M, K, N) in ((512, 5120, 34816), (512, 17408, 5120), (2048, 5120, 34816), (4096, 8192, 8192)):
-        L = synth.LayerInputs(0, 3, 1, K, N)
+        L = synth.LayerInputs(0, S_PRE, 1, K, N)
         codes = L.codes_torch(dev)
         scales = torch.from_numpy(L.scales()).to(dev)
         packed, q, rs = tl.pack_weights(codes, scales)
@@ -720,7 +724,8 @@ def library_reference(tl, torch, dev, n=20):
 
 
 SWEEP_BS = (1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48, 64, 96, 128, 192, 256, 384, 512)
-SWEEP_SHAPES = (("qkv", 1, 0, 5120, 10240), ("gate_up", 2, 0, 5120, 34816), ("down", 2, 1, 17408, 5120))
+SWEEP_SHAPES = (("qkv", "decode_qkv", 0, 5120, 10240), ("gate_up", "decode_mlp", 0, 5120, 34816),
+                ("down", "decode_mlp", 1, 17408, 5120))
 
 
 def bsweep(tl, torch, dev, log, n=20):
@@ -745,8 +750,9 @@ def bsweep(tl, torch, dev, log, n=20):
     spin_ms_per_m = e0.elapsed_time(e1)
     spin = int(1_000_000 * (n * 0.2) / spin_ms_per_m)      # about 200 us of device spin per layer
     print(json.dumps({"spin_cycles": spin, "spin_ms": round(spin * spin_ms_per_m / 1e6, 2)}), flush=True)
-    for name, config, li, K, N in SWEEP_SHAPES:
-        L = synth.LayerInputs(0, config, li, K, N)
+    for name, wl, li, K, N in SWEEP_SHAPES:
+        stream = synth.WORKLOADS[wl]["stream"]
+        L = synth.LayerInputs(0, stream, li, K, N)
         codes = L.codes_torch(dev)
         scales = torch.from_numpy(L.scales()).to(dev)
         packed, q, rs = tl.pack_weights(codes, scales)
@@ -755,7 +761,7 @@ def bsweep(tl, torch, dev, log, n=20):
         R = max(2, math.ceil(ROTATE_BYTES / per))
         copies = [(packed, scales, q, rs)] + [(packed.clone(), scales.clone(), q.clone(), rs.clone())
                                               for _ in range(R - 1)]
-        x_all = bf16(synth.activations(0, config, 100 + li, max(SWEEP_BS), K))
+        x_all = bf16(synth.activations(0, stream, 100 + li, max(SWEEP_BS), K))
         rows = []
         for T in SWEEP_BS:
             x = x_all[:T]
@@ -830,13 +836,14 @@ def stack_pass(tl, torch, dev, steps, log):
     the whole-pass times.
     """
     import synth
-    types = [(name, K, N) for name, K, N in synth.CONFIGS[4]["layers"]]
-    blocks = synth.CONFIGS[4]["blocks"]
+    types = [(name, K, N) for name, K, N in synth.WORKLOADS["stack64"]["layers"]]
+    blocks = synth.WORKLOADS["stack64"]["blocks"]
+    s_stack = synth.WORKLOADS["stack64"]["stream"]
     layers = []
     packed_bytes = 0
     for blk in range(blocks):
         for ti, (name, K, N) in enumerate(types):
-            L = synth.LayerInputs(0, 4, 4 * blk + ti, K, N)
+            L = synth.LayerInputs(0, s_stack, 4 * blk + ti, K, N)
             codes = L.codes_torch(dev)
             scales = torch.from_numpy(L.scales()).to(dev)
             packed, q, rs = tl.pack_weights(codes, scales)
@@ -848,8 +855,8 @@ def stack_pass(tl, torch, dev, steps, log):
     B, M = 16, 2048
     io = []
     for ti, (name, K, N) in enumerate(types):
-        io.append(dict(K=K, N=N, xd=bf16(synth.activations(0, 4, ti, B, K)),
-                       xp=bf16(synth.activations(0, 4, len(types) + ti, M, K)),
+        io.append(dict(K=K, N=N, xd=bf16(synth.activations(0, s_stack, ti, B, K)),
+                       xp=bf16(synth.activations(0, s_stack, len(types) + ti, M, K)),
                        ws=torch.empty((tl.gemv_workspace_size(B, K, N),), dtype=torch.uint8, device=dev),
                        yd=torch.empty((B, N), dtype=torch.bfloat16, device=dev),
                        xq=torch.empty((M, K), dtype=torch.int8, device=dev),
@@ -933,7 +940,7 @@ def phase_stamps(tl, torch, dev, layers, bf16, synth):
     out = {}
     for name, (copies, K, N) in layers.items():
         for b in DECODE_BS:
-            x = bf16(synth.activations(0, 1, 0, b, K))
+            x = bf16(synth.activations(0, S_DEC, 0, b, K))
             ws = torch.empty((tl.gemv_workspace_size(b, K, N),), dtype=torch.uint8, device=dev)
             y = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
             tl.gemv_prepare_x(x, ws)
@@ -1016,7 +1023,7 @@ def cpu_baseline(seconds):
     import synth
     blas = [i for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas"]
     threads = max(i["num_threads"] for i in blas) if blas else (os.cpu_count() or 1)
-    L = synth.LayerInputs(0, 1, 0, 5120, 10240)
+    L = synth.LayerInputs(0, S_DEC, 0, 5120, 10240)
     codes, scales = L.codes(), L.scales()
     x = synth.bf16_bits_to_f32(L.x(16))
 
@@ -1029,10 +1036,10 @@ def cpu_baseline(seconds):
     db = gemv_bytes(16, 5120, 10240)
     prefill = {}
     for name, li, K, N in (("gate_up", 0, 5120, 34816), ("down", 1, 17408, 5120)):
-        Lp = synth.LayerInputs(0, 3, li, K, N)
+        Lp = synth.LayerInputs(0, S_PRE, li, K, N)
         pc, ps = Lp.codes(), Lp.scales()
         q, rs, _ = oracle.decompose_scales(ps)
-        xp = synth.bf16_bits_to_f32(synth.activations(0, 3, li, PREFILL_M, K))
+        xp = synth.bf16_bits_to_f32(synth.activations(0, S_PRE, li, PREFILL_M, K))
 
         def pre(xs):
             xq, sx = oracle.quant_act_int8(oracle.rotate_f32(xs))

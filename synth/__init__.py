@@ -21,7 +21,8 @@ Codes come from a counter-based generator (murmur3's 32-bit finaliser applied
 twice to the element index, keyed per layer) so that any row of any layer can
 be regenerated on its own, on the host with numpy or on the device with torch,
 bit-identically.  Scales and activations use numpy's PCG64 with a SeedSequence
-keyed by (seed, config, layer, tensor).
+keyed by (seed, stream, layer, tensor); a stream is the number of one workload's
+random streams (see WORKLOADS).
 """
 from __future__ import annotations
 
@@ -100,14 +101,14 @@ def ternary_codes_torch(key: int, row0: int, nrows: int, K: int, device="cpu"):
 # ---------------------------------------------------------------------------
 # scales and activations
 # ---------------------------------------------------------------------------
-def _rng(seed: int, config: int, layer: int, tensor: int) -> np.random.Generator:
-    ss = np.random.SeedSequence(entropy=seed, spawn_key=(config, layer, tensor))
+def _rng(seed: int, stream: int, layer: int, tensor: int) -> np.random.Generator:
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(stream, layer, tensor))
     return np.random.Generator(np.random.PCG64(ss))
 
 
-def group_scales(seed: int, config: int, layer: int, N: int, K: int) -> np.ndarray:
+def group_scales(seed: int, stream: int, layer: int, N: int, K: int) -> np.ndarray:
     """fp16 scales [N, K/128], lognormal(-4, 0.5) rounded to nearest fp16."""
-    rng = _rng(seed, config, layer, TENSOR_SCALES)
+    rng = _rng(seed, stream, layer, TENSOR_SCALES)
     z = rng.standard_normal((N, K // GROUP))
     return np.exp(-4.0 + 0.5 * z).astype(np.float16)
 
@@ -123,15 +124,15 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def outlier_channels(seed: int, config: int, layer: int, K: int) -> np.ndarray:
-    rng = _rng(seed, config, layer, TENSOR_X)
+def outlier_channels(seed: int, stream: int, layer: int, K: int) -> np.ndarray:
+    rng = _rng(seed, stream, layer, TENSOR_X)
     n_out = int(round(0.005 * K))
     return np.sort(rng.permutation(K)[:n_out])
 
 
-def activations(seed: int, config: int, layer: int, T: int, K: int) -> np.ndarray:
+def activations(seed: int, stream: int, layer: int, T: int, K: int) -> np.ndarray:
     """bf16 bit patterns [T, K]: N(0,1) with 0.5% of channels scaled by 20."""
-    rng = _rng(seed, config, layer, TENSOR_X)
+    rng = _rng(seed, stream, layer, TENSOR_X)
     n_out = int(round(0.005 * K))
     chans = np.sort(rng.permutation(K)[:n_out])
     z = rng.standard_normal((T, K))
@@ -152,21 +153,23 @@ LAYER_SHAPES = {
     "down": (17408, 5120),
 }
 
-CONFIGS = {
-    0: dict(name="tiny", layers=[("tiny", 1024, 256)], decode_b=[1], prefill_m=[1]),
-    1: dict(name="decode_qkv", layers=[("qkv", 5120, 10240)], decode_b=[1, 4, 8, 16], prefill_m=[]),
-    2: dict(name="decode_mlp", layers=[("gate_up", 5120, 34816), ("down", 17408, 5120)],
-            decode_b=[1, 16], prefill_m=[]),
-    3: dict(name="prefill_mlp", layers=[("gate_up", 5120, 34816), ("down", 17408, 5120)],
-            decode_b=[], prefill_m=[512]),
-    4: dict(name="stack64", blocks=64, layers=[(n, *LAYER_SHAPES[n]) for n in ("qkv", "o", "gate_up", "down")],
-            decode_b=[16], prefill_m=[2048]),
+# the workloads, by name; `stream` numbers each one's random streams (the
+# inputs of workload w, layer l come from streams (seed, w["stream"], l, tensor))
+WORKLOADS = {
+    "tiny": dict(stream=0, layers=[("tiny", 1024, 256)], decode_b=[1], prefill_m=[1]),
+    "decode_qkv": dict(stream=1, layers=[("qkv", 5120, 10240)], decode_b=[1, 4, 8, 16], prefill_m=[]),
+    "decode_mlp": dict(stream=2, layers=[("gate_up", 5120, 34816), ("down", 17408, 5120)],
+                       decode_b=[1, 16], prefill_m=[]),
+    "prefill_mlp": dict(stream=3, layers=[("gate_up", 5120, 34816), ("down", 17408, 5120)],
+                        decode_b=[], prefill_m=[512]),
+    "stack64": dict(stream=4, blocks=64, layers=[(n, *LAYER_SHAPES[n]) for n in ("qkv", "o", "gate_up", "down")],
+                    decode_b=[16], prefill_m=[2048]),
 }
 
 
-def layer_key(seed: int, config: int, layer: int) -> int:
-    """64-bit key of the code generator for one layer of one config."""
-    ss = np.random.SeedSequence(entropy=seed, spawn_key=(config, layer, TENSOR_CODES))
+def layer_key(seed: int, stream: int, layer: int) -> int:
+    """64-bit key of the code generator for one layer of one workload stream."""
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(stream, layer, TENSOR_CODES))
     w = ss.generate_state(2, dtype=np.uint32)
     return int(w[0]) | (int(w[1]) << 32)
 
@@ -174,9 +177,9 @@ def layer_key(seed: int, config: int, layer: int) -> int:
 class LayerInputs:
     """Inputs of one ternary linear layer: codes [N,K] int8, scales [N,K/128] fp16."""
 
-    def __init__(self, seed: int, config: int, layer: int, K: int, N: int):
-        self.seed, self.config, self.layer, self.K, self.N = seed, config, layer, K, N
-        self.key = layer_key(seed, config, layer)
+    def __init__(self, seed: int, stream: int, layer: int, K: int, N: int):
+        self.seed, self.stream, self.layer, self.K, self.N = seed, stream, layer, K, N
+        self.key = layer_key(seed, stream, layer)
 
     def codes(self, row0: int = 0, nrows: int | None = None) -> np.ndarray:
         nrows = self.N - row0 if nrows is None else nrows
@@ -187,7 +190,7 @@ class LayerInputs:
         return ternary_codes_torch(self.key, row0, nrows, self.K, device)
 
     def scales(self) -> np.ndarray:
-        return group_scales(self.seed, self.config, self.layer, self.N, self.K)
+        return group_scales(self.seed, self.stream, self.layer, self.N, self.K)
 
     def x(self, T: int) -> np.ndarray:
-        return activations(self.seed, self.config, self.layer, T, self.K)
+        return activations(self.seed, self.stream, self.layer, T, self.K)

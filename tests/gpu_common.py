@@ -47,8 +47,8 @@ def poison_(t):
 class Layer:
     """Host and device copies of one synthetic ternary layer."""
 
-    def __init__(self, seed, config, layer, K, N, d):
-        self.L = synth.LayerInputs(seed, config, layer, K, N)
+    def __init__(self, seed, stream, layer, K, N, d):
+        self.L = synth.LayerInputs(seed, stream, layer, K, N)
         self.K, self.N = K, N
         self.codes = self.L.codes()
         self.scales = self.L.scales()

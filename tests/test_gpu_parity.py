@@ -25,12 +25,12 @@ def tl():
     return tl
 
 
-# (config, layer index, K, N) of every layer shape in the workloads
+# (random stream of the workload, layer index, K, N) of every layer shape in the workloads
 SHAPES = {
-    "tiny": (0, 0, 1024, 256),
-    "qkv": (1, 0, 5120, 10240),
-    "gate_up": (2, 0, 5120, 34816),
-    "down": (2, 1, 17408, 5120),
+    "tiny": (synth.WORKLOADS["tiny"]["stream"], 0, 1024, 256),
+    "qkv": (synth.WORKLOADS["decode_qkv"]["stream"], 0, 5120, 10240),
+    "gate_up": (synth.WORKLOADS["decode_mlp"]["stream"], 0, 5120, 34816),
+    "down": (synth.WORKLOADS["decode_mlp"]["stream"], 1, 17408, 5120),
 }
 
 _layers = {}
