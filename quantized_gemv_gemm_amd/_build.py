@@ -33,7 +33,7 @@ DEVICE = [
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 # device assembly of the sources whose kernels count their own memory waits (read
 # by the CPU tests: every counted wait must cover the loads it claims to)
-ASM_SOURCES = ("k_gemv.hip",)
+ASM_SOURCES = ("k_gemv.hip", "k_gemm.hip")
 _FIELDS = {"TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
            "Occupancy [waves/SIMD]": "occupancy", "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
            "LDS Size [bytes/block]": "lds"}

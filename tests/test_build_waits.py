@@ -22,10 +22,9 @@ PKG = os.path.join(ROOT, "quantized_gemv_gemm_amd")
 KERNELS = ("gemv_stream_kernel", "gemv_q8_kernel", "gemv_rot_kernel")
 
 
-@pytest.fixture(scope="module")
-def listing():
+def _read_listing(src):
     from quantized_gemv_gemm_amd import _build
-    path = _build.asm_path("k_gemv.hip")
+    path = _build.asm_path(src)
     srcs = [os.path.join(PKG, "csrc", f) for f in os.listdir(os.path.join(PKG, "csrc"))]
     if not os.path.exists(path) or os.path.getmtime(path) < max(os.path.getmtime(s) for s in srcs):
         _build.build()
@@ -33,8 +32,18 @@ def listing():
         return f.read()
 
 
-def _functions(text):
-    pat = r"^(_ZN2tl[^:\n]*(?:%s)[^:\n]*):[^\n]*\n(.*?)^\.Lfunc_end" % "|".join(KERNELS)
+@pytest.fixture(scope="module")
+def listing():
+    return _read_listing("k_gemv.hip")
+
+
+@pytest.fixture(scope="module")
+def gemm_listing():
+    return _read_listing("k_gemm.hip")
+
+
+def _functions(text, kernels=KERNELS):
+    pat = r"^(_ZN2tl[^:\n]*(?:%s)[^:\n]*):[^\n]*\n(.*?)^\.Lfunc_end" % "|".join(kernels)
     for name, body in re.findall(pat, text, re.S | re.M):
         lines = []
         for raw in body.split("\n"):
@@ -117,3 +126,54 @@ def test_checker_flags_a_short_count():
     for name, lines in _functions(fake):
         found[name.split("N_")[1][:10]] = _claim_and_loads(name, lines)
     assert found == {"118gemv_st": (3, 2), "114gemv_q8": (2, 1)}
+
+
+# The GEMM's pair loop: the next pair's activation stage is copied into LDS with
+# direct loads at the start of the pair, the weight words of pair p + 2 are
+# loaded at its last k-step, and the pair ends with s_waitcnt vmcnt(4 J) and the
+# workgroup barrier: the stage must have landed, the 4 J weight loads (two
+# 16-byte code loads and two scale bytes per weight column) may stay in flight.
+
+
+def _gemm_waits(lines):
+    """(N, loads after the last direct load, a direct load in the block) for every
+    vmcnt(N) wait, 0 < N < 63, that a barrier follows."""
+    out = []
+    for i, line in enumerate(lines):
+        if not (line.startswith("s_barrier") and i and lines[i - 1].startswith("s_waitcnt")):
+            continue
+        m = re.search(r"vmcnt\((\d+)\)", lines[i - 1])
+        if not m or not 0 < int(m.group(1)) < 63:
+            continue
+        w = i - 1
+        start = max([j for j in range(w) if lines[j].endswith(":") or _is_dma(lines[j])], default=-1)
+        out.append((int(m.group(1)), sum(1 for l in lines[start + 1:w] if _is_load(l)),
+                    start >= 0 and _is_dma(lines[start])))
+    return out
+
+
+def test_gemm_counted_waits_cover_their_loads(gemm_listing):
+    checked, bad = 0, []
+    for name, lines in _functions(gemm_listing, ("gemm_i8_kernel",)):
+        for n, loads, dma in _gemm_waits(lines):
+            checked += 1
+            if not dma or loads < n:
+                bad.append(f"{name[:60]}: vmcnt({n}) after {loads} loads (direct load in the block: {dma})")
+    assert checked >= 8
+    assert not bad, "\n".join(bad[:10])
+
+
+def test_gemm_checker_flags_a_short_count():
+    """A pair whose weight loads were moved above its direct loads is reported."""
+    fake = (
+        "_ZN2tl12_GLOBAL__N_114gemm_i8_kernelILb1EEEv: ; @z\n"
+        "\tbuffer_load_dwordx4 v[6:9], v1, s[0:3], 0 offen\n"
+        "\tbuffer_load_dwordx4 v168, s[28:31], s55 offen lds\n"
+        "\tv_mfma_i32_32x32x32_i8 v[18:33], v[226:229], v[130:133], v[18:33]\n"
+        "\tbuffer_load_ubyte v2, v3, s[4:7], 0 offen\n"
+        "\ts_waitcnt vmcnt(2)\n"
+        "\ts_barrier\n"
+        "\ts_endpgm\n"
+        ".Lfunc_end2:\n")
+    ((name, lines),) = list(_functions(fake, ("gemm_i8_kernel",)))
+    assert _gemm_waits(lines) == [(2, 1, True)]
