@@ -129,6 +129,8 @@ def test_gemm_rejections():
     assert L.tl_gemm_int8_rescale(*args(y=FAKE, K=128)) == 8   # one pair of groups: no workspace
     assert L.tl_gemm_int8_rescale(*args(y=FAKE)) == 7            # 8 x 1024 x 256 is split along K
     assert L.tl_gemm_int8_rescale(*args(M=0)) == 0
+    assert L.tl_gemm_int8_rescale(*args(N=0)) == 0
+    assert L.tl_gemm_int8_rescale(*args(M=-1)) == 2
     # 512 x 40960 leaves 128 of 640 tiles for a last round: they are split along K;
     # 512 x 34816 leaves 32 of 544, cut into sub-tiles that need no workspace
     need = L.tl_gemm_workspace_size(512, 5120, 40960)
