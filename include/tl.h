@@ -253,7 +253,8 @@ int tl_quant_act_int8(const float *xr, int64_t T, int64_t K, int8_t *xq, float *
  *     tl_gemv_ternary_x   == tl_hadamard_blk then tl_gemv_ternary
  *     tl_quant_act_int8_x == tl_hadamard_blk then tl_quant_act_int8
  *   except tl_gemv_ternary_x (and the GEMV path of tl_linear_apply) for one
- *   token with N <= 12288 or two tokens with N <= 6144, and K <= 6144: there a
+ *   token with N <= 12288 and K <= 6144 (N <= 8192 at K = 6144) or two tokens
+ *   with N <= 6144 and K <= 4096, K a multiple of 1024: there a
  *   single kernel rotates, splits into limbs and runs the GEMV, each workgroup
  *   rotating the blocks it needs; its limbs are the same, but it adds the
  *   group results in another order, so its output is not bit-identical to the

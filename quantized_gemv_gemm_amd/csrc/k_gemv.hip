@@ -1493,12 +1493,20 @@ hipError_t launch_gemv_main(const void *workspace, int64_t b, int64_t K, int64_t
 
 // The one-launch path trades redundant rotations (every workgroup rotates every
 // block of every token) for one launch fewer and no limb round trip, so it is
-// ahead while the workgroups are few.  Measured (device time, K = 5120) against
-// prep + GEMV: one token 9.1 vs 11.0 us at N = 10240, 6.7 vs 9.6 at 5120, behind
-// at 34816; two tokens 9.6 vs 10.0 at N = 5120, behind at 10240.
+// ahead while the workgroups and the rotations per wave are few.  Measured
+// against the fused prep + GEMV pair (back-to-back launches over rotating weight
+// copies, us, one launch vs two):
+//  * one token: ahead at every K <= 6144 and N <= 12288 but one (K = 5120:
+//    5.8 vs 6.9 at N = 1024, 9.1 vs 9.4 at 10240, 9.3 vs 9.4 at 12288; K = 6144:
+//    7.6 vs 9.3 at N = 8192, behind at 12288, 10.8 vs 10.4), and behind at
+//    N = 34816;
+//  * two tokens: ahead while K <= 4096 (K = 2048: 5.5 vs 6.5 at N = 1024, 6.7 vs
+//    7.3 at 6144; K = 4096: 6.4 vs 6.8 at 1024, 7.8 vs 7.9 at 6144), behind from
+//    K = 5120 on (7.9 vs 7.1 at N = 1024, 9.4 vs 8.3 at 5120).
 bool gemv_rot_supported(int64_t b, int64_t K, int64_t N) {
   if (K <= 0 || K % kHBlock || K / kHBlock > kRotMaxBlocks) return false;
-  return (b == 1 && N <= 12288) || (b == 2 && N <= 6144);
+  if (b == 1) return N <= 12288 && (K <= 5120 || N <= 8192);
+  return b == 2 && N <= 6144 && K <= 4096;
 }
 
 hipError_t launch_gemv_rot(const uint16_t *x, int64_t b, int64_t K, int64_t N, const int8_t *signs,

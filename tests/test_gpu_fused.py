@@ -97,7 +97,7 @@ def test_gemv_prepare_fused_bitexact(tl, K, b, signed):
 
 
 @pytest.mark.parametrize("K,N,b", [(5120, 1000, 1), (5120, 10240, 8), (17408, 512, 2),
-                                   (5120, 1000, 33), (3072, 300, 64)])
+                                   (5120, 1000, 33), (3072, 300, 64), (2048, 1000, 2), (5120, 3000, 2)])
 def test_gemv_ternary_fused_matches(tl, K, N, b):
     import torch
     d = dev()

@@ -212,7 +212,8 @@ def test_gemv_parity(tl, name, b):
 
 
 @pytest.mark.parametrize("K,N,b", [(128, 300, 3), (256, 17, 16), (1024, 1000, 5), (3072, 64, 2),
-                                   (384, 33, 8), (17408, 48, 1), (5120, 100, 12),
+                                   (384, 33, 8), (17408, 48, 1), (5120, 100, 12), (13440, 40, 1),
+                                   (17024, 70, 2),
                                    (256, 17, 17), (1024, 1000, 31), (384, 33, 50), (17408, 48, 64)])
 def test_gemv_ragged(tl, K, N, b):
     """N not a multiple of the row tile, K smaller than the wave count, odd b."""
@@ -238,6 +239,7 @@ def test_gemv_ragged(tl, K, N, b):
 
 
 @pytest.mark.parametrize("K,N,b", [(5120, 300, 4), (5120, 300, 16), (2304, 1000, 16), (17408, 200, 1),
+                                   (17024, 70, 2), (13440, 40, 1),
                                    (17408, 200, 16), (3200, 64, 8)])
 def test_gemv_block_scales(tl, K, N, b):
     """Activations whose 1024-blocks differ wildly in size: a block of zeros
