@@ -32,7 +32,8 @@ def _layer(tl, d, K, N, seed):
 
 @pytest.mark.parametrize("T,K,N,signed", [(1, 5120, 1000, True), (2, 3072, 5000, False),
                                           (5, 1024, 300, False), (40, 2048, 1000, True), (64, 1024, 77, False),
-                                          (80, 1024, 300, True), (17, 1024, 20544, False), (200, 3072, 129, False)])
+                                          (80, 1024, 300, True), (17, 1024, 20544, False), (200, 3072, 129, False),
+                                          (2, 5120, 1000, False), (1, 6144, 10000, True), (2, 4096, 6144, True)])
 def test_linear_apply(tl, T, K, N, signed):
     import torch
     d = dev()
@@ -84,3 +85,25 @@ def test_linear_workspace_shared_across_paths(tl):
         else:
             first[T] = y.cpu().numpy()
     assert int(ws[:1024].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("T,K,N,one_launch", [(1, 5120, 10240, True), (1, 6144, 8192, True), (1, 6144, 12288, False),
+                                               (1, 5120, 12289, False), (2, 4096, 6144, True), (2, 5120, 1000, False),
+                                               (2, 2048, 6145, False), (3, 1024, 256, False)])
+def test_one_launch_rule(tl, T, K, N, one_launch):
+    """The decode layer runs as one launch (rotation in every workgroup) exactly
+    where the measured rule says it is ahead of the fused prep + GEMV pair: one
+    token up to N = 12288 (8192 at K = 6144), two tokens up to N = 6144 while
+    K <= 4096."""
+    import torch
+    d = dev()
+    codes, scales, sd, packed, q, rs = _layer(tl, d, K, N, T * 7 + K + N)
+    x = bf16_dev(synth.activations(0, 1, 13, T, K), d)
+    announce(f"one-launch rule T={T} K={K} N={N}")
+    y = tl.linear_apply(x, packed, sd, q, rs, out_dtype=torch.float32)
+    kname = tl.last_kernel_name()
+    torch.cuda.synchronize()
+    assert kname.startswith("gemv_rot") == one_launch, kname
+    ref = oracle.gemv_ternary(oracle.rotate_exact(synth.bf16_bits_to_f32(synth.activations(0, 1, 13, T, K))),
+                              codes, scales)
+    assert oracle.rel_fro(y.cpu().numpy(), ref) <= REL_TOL
