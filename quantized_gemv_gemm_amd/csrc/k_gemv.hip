@@ -629,7 +629,9 @@ __global__ __launch_bounds__(stream_threads(ALDS, RB, PMAX, LP)) void gemv_strea
       for (int i = 0; i < NT; ++i) acc[rb][i] *= ua[i];
   }
   ps.flush();
-  __syncthreads();  // every wave is done with LDS before `red` is written
+  // `red` lies past every region the loop reads (limbs, scales, limb scales), and
+  // every direct load into LDS was waited for before the first barrier: the
+  // partials can go to LDS at once, the barrier inside the reduction orders them
   reduce_and_store<RB, NT, LP>(acc, red, W, wave, lane, b, n0, N, tsc, y, y_dtype);
   ps.done();
 }
