@@ -79,6 +79,8 @@ def parse():
                         "shapes, with int8 weights already expanded, beside this library's GEMM")
     p.add_argument("--calib-copy", action="store_true",
                    help="only run a 64 MiB device copy 20 times (the PMC byte-counter calibration)")
+    p.add_argument("--warm", action="store_true",
+                   help="with --phase-stamps: one weight copy (Infinity-Cache resident) instead of rotating copies")
     p.add_argument("--phase-stamps", action="store_true",
                    help="load the instrumented library (python -m quantized_gemv_gemm_amd._build --phase-stamps) "
                         "and print the decode GEMV's per-wave phase times at qkv and gate_up, b = 1, 4, 8, 16")
@@ -348,7 +350,11 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     if args.phase_stamps:
-        phase_stamps(tl, torch, dev, {"qkv": (qkv, 5120, 10240), "gate_up": (gate_up, 5120, 34816)}, bf16, synth)
+        if args.warm:   # a diagnostic: the weights served from the Infinity Cache, not HBM
+            phase_stamps(tl, torch, dev, {"qkv_warm": (qkv[:1], 5120, 10240), "gate_up_warm": (gate_up[:1], 5120, 34816)},
+                         bf16, synth)
+        else:
+            phase_stamps(tl, torch, dev, {"qkv": (qkv, 5120, 10240), "gate_up": (gate_up, 5120, 34816)}, bf16, synth)
         return
 
     Kq, Nq = 5120, 10240
